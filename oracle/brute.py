@@ -1,0 +1,52 @@
+"""Brute-force dense check of the oracle -- TEST INFRASTRUCTURE ONLY.
+
+An implementation independent of oracle.c, for tiny inputs: rows are
+dequantised with PyTorch's own float8_e4m3fn and bfloat16 conversions (not the
+oracle's decoder), logits come from one dense fp64 matrix product over the
+gathered rows, and the softmax from scipy's logsumexp.  It follows the same
+definition: attention of each head over the rows its top-k list selects, with
+keys and values equal to the dequantised 512-wide latent row.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+from scipy.special import logsumexp
+
+
+def dequant_rows_torch(rows: np.ndarray) -> np.ndarray:
+    """rows uint8 [N,640] -> K fp64 [N,512] using torch's dtype conversions."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    n = rows.shape[0]
+    t = torch.from_numpy(rows)
+    codes = t[:, :448].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    scales = t[:, 448:476].contiguous().view(torch.float32).to(torch.float64)  # [N,7]
+    nope = codes * scales.repeat_interleave(64, dim=1)
+    rope = t[:, 480:608].contiguous().view(torch.bfloat16).to(torch.float64)
+    return torch.cat([nope, rope], dim=1).numpy().reshape(n, 512)
+
+
+def q_values(q_bits: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(q_bits, dtype=np.uint16).view(np.int16)) \
+        .view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def brute_decode(q_bits, cache, kv_seq_stride, idx, seqlens, scale):
+    """Dense fp64 attention restricted to the selected rows (tiny inputs)."""
+    q = q_values(q_bits)                       # [B,H,512]
+    B, H, _ = q.shape
+    cache = cache.reshape(B, kv_seq_stride, 640)
+    out = np.zeros((B, H, 512))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        sel = [int(t) for t in idx[b] if 0 <= t < seqlens[b]]
+        if not sel:
+            continue
+        K = dequant_rows_torch(cache[b, sel])  # [n,512]
+        z = scale * (q[b] @ K.T)               # [H,n]
+        l = logsumexp(z, axis=1)
+        p = np.exp(z - l[:, None])
+        out[b] = p @ K
+        lse[b] = l
+    return out, lse

@@ -1,0 +1,194 @@
+"""Pins of the fp64 CPU oracle against things other than itself: an
+independent dense brute-force computation, closed forms, invariants and the
+padded-512 formulation of the pages (which must agree bit for bit)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.brute import brute_decode, dequant_rows_torch, q_values
+from workloads import build_host_cache, config_workload, make_workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run(w, **kw):
+    cache = build_host_cache(w)
+    out, lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads,
+                                    w.scale, **kw)
+    return out, lse, cache
+
+
+TINY = [
+    dict(seed=11, batch=1, heads=16, topk=16, seqlen=64),
+    dict(seed=12, batch=2, heads=16, topk=16, seqlen=40),
+    dict(seed=13, batch=2, heads=4 * 4, topk=8, seqlens=[5, 64], structure="ragged"),
+    dict(seed=14, batch=2, heads=16, topk=16, seqlen=64, q_mult=4.0),
+    dict(seed=15, batch=1, heads=16, topk=16, seqlen=16),
+]
+
+
+@pytest.mark.parametrize("cfg", TINY)
+def test_oracle_matches_brute_force(cfg):
+    w = make_workload(**cfg)
+    out, lse, cache = run(w)
+    bout, blse = brute_decode(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.scale)
+    scale = max(1.0, np.abs(bout).max())
+    assert np.abs(out - bout).max() <= 1e-12 * scale
+    fin = np.isfinite(blse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.abs(lse[fin] - blse[fin]).max() <= 1e-12 * max(1.0, np.abs(blse[fin]).max())
+
+
+@pytest.mark.parametrize("cfg", TINY + [dict(seed=21, batch=2, heads=16, topk=64, seqlen=256)])
+def test_padded512_formulation_is_bitwise_equal(cfg):
+    # columns 448..511 padded with zeros and mapped to the (NaN-filled) pad
+    # scale slot, excluded by selection: results must be identical bits
+    w = make_workload(**cfg)
+    out, lse, cache = run(w)
+    sel = cache.reshape(-1, 640)[w.idx[0]]
+    assert np.all(np.isnan(sel[:, 476:480].copy().view(np.float32)))   # pad slot holds NaN
+    pout, plse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens,
+                                      w.heads, w.scale, padded512=True)
+    assert np.array_equal(out.view(np.uint64), pout.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), plse.view(np.uint64))
+
+
+def test_pad_slot_is_never_read():
+    # the generator fills scale slot 7 and bytes 608..639 with 0xFF (NaN);
+    # any read of them would turn outputs into NaN
+    w = make_workload(seed=5, batch=2, heads=16, topk=32, seqlen=128)
+    out, lse, cache = run(w)
+    rows = cache.reshape(-1, 640)
+    used = rows[w.idx[0]]
+    assert np.all(used[:, 476:480] == 0xFF) and np.all(used[:, 608:] == 0xFF)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_masked_entries_change_nothing():
+    # inserting -1 and out-of-range entries anywhere leaves results bitwise equal
+    w = make_workload(seed=31, batch=2, heads=16, topk=24, seqlen=100)
+    out, lse, cache = run(w)
+    rng = np.random.default_rng(0)
+    extra = np.array([[-1, 100, 5000, -7], [-2, 101, -1, 2 ** 30]], dtype=np.int32)
+    idx2 = np.concatenate([w.idx, extra], axis=1)
+    for b in range(2):
+        perm_pos = rng.permutation(idx2.shape[1])
+        # keep the valid entries in their original relative order
+        valid = [v for v in idx2[b] if 0 <= v < 100]
+        junk = [v for v in idx2[b] if not (0 <= v < 100)]
+        slots = sorted(perm_pos[:len(junk)])
+        row, vi, ji = [], 0, 0
+        for pos in range(idx2.shape[1]):
+            if ji < len(junk) and pos == slots[ji]:
+                row.append(junk[ji]); ji += 1
+            else:
+                row.append(valid[vi]); vi += 1
+        idx2[b] = row
+    out2, lse2, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, idx2, w.seqlens, w.heads, w.scale)
+    assert np.array_equal(out.view(np.uint64), out2.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), lse2.view(np.uint64))
+
+
+def test_permutation_invariance():
+    w = make_workload(seed=32, batch=2, heads=16, topk=64, seqlen=512, q_mult=4.0)
+    out, lse, cache = run(w)
+    idx2 = np.ascontiguousarray(np.random.default_rng(1).permuted(w.idx, axis=1))
+    out2, lse2, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, idx2, w.seqlens, w.heads, w.scale)
+    assert np.abs(out - out2).max() <= 1e-13 * max(1, np.abs(out).max())
+    assert np.abs(lse - lse2).max() <= 1e-13 * max(1, np.abs(lse).max())
+
+
+def test_single_token_returns_its_row():
+    w = make_workload(seed=33, batch=2, heads=16, topk=8, seqlens=[1, 300], kv_seq_stride=300)
+    w.idx[:] = -1
+    w.idx[0, 3] = 0
+    w.idx[1, 5] = 123
+    out, lse, cache = run(w)
+    rows = cache.reshape(2, 300, 640)
+    K0 = dequant_rows_torch(rows[0, [0]])[0]
+    K1 = dequant_rows_torch(rows[1, [123]])[0]
+    q = q_values(w.q_bits)
+    assert np.array_equal(out[0], np.broadcast_to(K0, out[0].shape))
+    assert np.array_equal(out[1], np.broadcast_to(K1, out[1].shape))
+    assert np.allclose(lse[0], w.scale * (q[0] @ K0), rtol=1e-13, atol=1e-13)
+    assert np.allclose(lse[1], w.scale * (q[1] @ K1), rtol=1e-13, atol=1e-13)
+
+
+def test_zero_query_gives_mean_and_log_count():
+    w = make_workload(seed=34, batch=2, heads=16, topk=32, seqlens=[20, 200], structure="ragged",
+                      kv_seq_stride=200)
+    w.q_bits[:] = 0
+    out, lse, cache = run(w)
+    for b in range(2):
+        sel = [t for t in w.idx[b] if 0 <= t < w.seqlens[b]]
+        K = dequant_rows_torch(cache.reshape(2, 200, 640)[b, sel])
+        assert np.allclose(out[b], K.mean(axis=0)[None], rtol=1e-13, atol=1e-13)
+        assert np.allclose(lse[b], np.log(len(sel)), rtol=0, atol=1e-14)
+
+
+def test_equal_logits_tie():
+    # q has only rope components; two rows share their rope but differ in nope:
+    # equal logits, so out is the plain mean and lse = z + ln 2
+    w = make_workload(seed=35, batch=1, heads=16, topk=2, seqlen=16)
+    w.q_bits[:, :, :448] = 0
+    cache = build_host_cache(w)
+    rows = cache.reshape(16, 640)
+    a, b = w.idx[0]
+    rows[b, 480:608] = rows[a, 480:608]
+    out, lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads, w.scale)
+    K = dequant_rows_torch(rows[[a, b]])
+    q = q_values(w.q_bits)[0]
+    z = w.scale * (q @ K[0])
+    assert np.allclose(out[0], ((K[0] + K[1]) / 2)[None], rtol=1e-14, atol=1e-14)
+    assert np.allclose(lse[0], z + np.log(2), rtol=1e-14, atol=1e-14)
+
+
+def test_empty_list():
+    w = make_workload(seed=36, batch=2, heads=16, topk=4, seqlens=[0, 10], kv_seq_stride=10)
+    w.idx[1] = [-1, 10, 11, -5]
+    out, lse, _ = run(w)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_large_scale_limit_selects_argmax_row():
+    w = make_workload(seed=37, batch=1, heads=16, topk=16, seqlen=64, scale=1e4)
+    out, lse, cache = run(w)
+    K = dequant_rows_torch(cache.reshape(64, 640)[w.idx[0]])
+    q = q_values(w.q_bits)[0]
+    z = q @ K.T
+    best = z.argmax(axis=1)
+    assert np.allclose(out[0], K[best], rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 3, 4, 7, 16, 40])
+def test_split_and_combine_equals_unsplit(nsplit):
+    # includes empty splits: the list has 32 entries of which a tail is -1
+    w = make_workload(seed=38, batch=2, heads=16, topk=32, seqlens=[12, 400], structure="ragged",
+                      kv_seq_stride=400, q_mult=4.0)
+    out, lse, cache = run(w)
+    o_p, l_p = oracle.decode_splits(w, nsplit, cache)
+    cout, clse = oracle.combine(o_p, l_p)
+    assert np.abs(cout - out).max() <= 1e-14 * max(1, np.abs(out).max())
+    assert np.abs(clse - lse).max() <= 1e-14 * max(1, np.abs(lse).max())
+
+
+def test_combine_all_empty():
+    o = np.random.default_rng(0).standard_normal((2, 3, 4, 512))
+    l = np.full((2, 3, 4), -np.inf)
+    out, lse = oracle.combine(o, l)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_golden_regression():
+    # values written by tests/golden/make_golden.py from the oracle
+    with open(os.path.join(GOLDEN, "oracle_cfg1.json")) as f:
+        g = json.load(f)
+    w = config_workload(1)
+    out, lse, _ = run(w)
+    assert np.allclose(lse.ravel(), np.array(g["lse"]), rtol=0, atol=1e-12)
+    sample = out.reshape(-1)[np.array(g["out_index"])]
+    assert np.allclose(sample, np.array(g["out_value"]), rtol=0, atol=1e-12)

@@ -1,0 +1,218 @@
+"""Seeded workload generator for sparse MLA decode (inputs only).
+
+Cache row byte layout (one latent KV row of a token, 640-byte stride):
+
+    bytes   0..447  448 "nope" values as fp8 e4m3fn codes (OCP; max 448)
+    bytes 448..475  7 fp32 group scales, group g covers nope columns 64g..64g+63
+    bytes 476..479  8th scale slot: padding, never read (filled with 0xFF = NaN)
+    bytes 480..607  64 "rope" values as bf16
+    bytes 608..639  padding (filled with 0xFF)
+
+The 448 + 64 split of the 512-wide latent row, the 7 groups of 64 columns plus
+one padding slot, and the fp8 nope / bf16 rope storage follow "The Power-of-Two
+Trap" (sections "The Scale Indexing Complication" and "Input Knowledge
+Required").  The group scale is amax/448 in fp32, the quantisation used by the
+synthetic workloads (the deployed model's power-of-two UE8M0 scales are a
+different format).
+
+Every cache row that no top-k entry selects, and every row past a sequence's
+length, is 0xFF bytes, which decodes as NaN in fp8, bf16 and fp32: a kernel
+that reads a row it should not read produces NaN.
+
+Draw order per workload: seqlens -> idx -> q -> nope -> rope, all from
+``numpy.random.Generator(PCG64(seed))``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+ROW_BYTES = 640
+NOPE = 448
+ROPE = 64
+LATENT = NOPE + ROPE
+GROUP = 64
+NGROUPS = NOPE // GROUP  # 7
+SCALE_OFF = 448
+ROPE_OFF = 480
+FP8_MAX = 448.0
+
+
+# --------------------------------------------------------------------------
+# value encoders (input preparation only)
+# --------------------------------------------------------------------------
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def encode_e4m3fn(v: np.ndarray) -> np.ndarray:
+    """Quantise to OCP fp8 e4m3fn codes: round to nearest even, saturate to +-448.
+
+    e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, no
+    infinities, only S.1111.111 is NaN, so the largest finite value is 448.
+    NaN inputs map to 0x7F.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    nan = np.isnan(v)
+    sign = np.signbit(v)
+    a = np.minimum(np.abs(np.where(nan, 0.0, v)), FP8_MAX)
+    _, e = np.frexp(a)                       # a = f * 2**e, f in [0.5, 1)
+    exp_unbiased = np.maximum(e - 1, -6)     # subnormals share exponent -6
+    quantum = np.ldexp(1.0, exp_unbiased - 3)
+    r = np.rint(a / quantum) * quantum       # np.rint: ties to even
+    # code from the rounded magnitude r (exactly representable)
+    _, er = np.frexp(r)
+    er = er - 1
+    normal = r >= 2.0 ** -6
+    mant_norm = np.where(normal, r / np.ldexp(1.0, er) * 8 - 8, 0)
+    code_norm = ((er + 7) << 3) + mant_norm.astype(np.int64)
+    code_sub = (r / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_norm, code_sub).astype(np.int64)
+    code = np.where(sign, code | 0x80, code)
+    code = np.where(nan, 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantise_rows(nope: np.ndarray, rope: np.ndarray) -> np.ndarray:
+    """Pack fp32 nope [N,448] and rope [N,64] into cache rows uint8 [N,640]."""
+    nope = np.ascontiguousarray(nope, dtype=np.float32)
+    rope = np.ascontiguousarray(rope, dtype=np.float32)
+    n = nope.shape[0]
+    g = nope.reshape(n, NGROUPS, GROUP)
+    amax = np.abs(g).max(axis=2)                                   # [N,7] fp32
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+    ratio = (g / scale[:, :, None]).astype(np.float32)             # fp32 x / s
+    codes = encode_e4m3fn(ratio).reshape(n, NOPE)
+    rows = np.full((n, ROW_BYTES), 0xFF, dtype=np.uint8)
+    rows[:, :NOPE] = codes
+    rows[:, SCALE_OFF:SCALE_OFF + 4 * NGROUPS] = scale.view(np.uint8).reshape(n, 4 * NGROUPS)
+    rows[:, ROPE_OFF:ROPE_OFF + 2 * ROPE] = bf16_bits_from_f32(rope).view(np.uint8).reshape(n, 2 * ROPE)
+    return rows
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    heads: int
+    topk: int
+    kv_seq_stride: int
+    scale: float              # softmax scale (a float32 value)
+    seqlens: np.ndarray       # int32 [B]
+    idx: np.ndarray           # int32 [B, topk]; -1 = padding
+    q_bits: np.ndarray        # uint16 [B, H, 512] bf16 bit patterns
+    rows: np.ndarray          # uint8 [B, topk, 640]: row of entry (b, j)
+    nsplits: tuple = (1,)     # split counts the parity tests use
+
+    @property
+    def valid(self) -> np.ndarray:
+        return (self.idx >= 0) & (self.idx < self.seqlens[:, None])
+
+    @property
+    def n_valid_rows(self) -> int:
+        return int(self.valid.sum())
+
+
+def _draw_idx(rng, seqlens, topk, structure):
+    B = len(seqlens)
+    idx = np.full((B, topk), -1, dtype=np.int32)
+    for b in range(B):
+        s = int(seqlens[b])
+        if structure == "uniform":
+            k = min(topk, s)
+            idx[b, :k] = rng.choice(s, size=k, replace=False)
+        elif structure == "recent20":
+            # 20 % of the list inside the last 512 positions, the rest uniform
+            # over the earlier positions, all distinct, then shuffled.
+            n_recent = int(round(0.2 * topk))
+            recent = s - 512 + rng.choice(512, size=n_recent, replace=False)
+            early = rng.choice(s - 512, size=topk - n_recent, replace=False)
+            row = np.concatenate([recent, early])
+            rng.shuffle(row)
+            idx[b] = row
+        elif structure == "ragged":
+            # all positions when the sequence is shorter than top-k, then -1
+            if s >= topk:
+                idx[b] = rng.choice(s, size=topk, replace=False)
+            else:
+                idx[b, :s] = rng.permutation(s)
+        else:
+            raise ValueError(structure)
+    return idx
+
+
+def make_workload(*, name="custom", seed=0, batch, heads, topk, seqlen=None,
+                  seqlens=None, kv_seq_stride=None, structure="uniform",
+                  q_mult=1.0, scale=None, nsplits=(1,)) -> Workload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if seqlens is None:
+        seqlens = np.full(batch, seqlen, dtype=np.int32)
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    assert seqlens.shape == (batch,)
+    if kv_seq_stride is None:
+        kv_seq_stride = int(seqlens.max()) if batch else 1
+    idx = _draw_idx(rng, seqlens, topk, structure)
+    q = rng.standard_normal((batch, heads, LATENT), dtype=np.float32) * np.float32(q_mult)
+    nope = rng.standard_normal((batch * topk, NOPE), dtype=np.float32)
+    rope = rng.standard_normal((batch * topk, ROPE), dtype=np.float32)
+    rows = quantise_rows(nope, rope).reshape(batch, topk, ROW_BYTES)
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(LATENT)))
+    return Workload(name=name, seed=seed, batch=batch, heads=heads, topk=topk,
+                    kv_seq_stride=int(kv_seq_stride), scale=float(np.float32(scale)),
+                    seqlens=seqlens, idx=idx, q_bits=bf16_bits_from_f32(q),
+                    rows=rows, nsplits=tuple(nsplits))
+
+
+def _cfg5_seqlens(seed):
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    s = rng.integers(1024, 131072, size=64, endpoint=True).astype(np.int32)
+    s[0] = 1024      # always exercises the -1 padding
+    s[1] = 131072    # always exercises the longest sequence
+    return s
+
+
+# The five synthetic workloads.  Shapes follow the decode setting of the
+# pages (one query token per sequence, 16 heads per GPU at TP=4 or all 64).
+CONFIGS = {
+    1: dict(name="tiny_b1_h16_s256_k64", batch=1, heads=16, topk=64, seqlen=256,
+            structure="uniform", nsplits=(1, 2)),
+    2: dict(name="b4_h16_s8192_k512", batch=4, heads=16, topk=512, seqlen=8192,
+            structure="uniform", nsplits=(4,)),
+    3: dict(name="b32_h64_s32768_k512", batch=32, heads=64, topk=512, seqlen=32768,
+            structure="uniform", nsplits=(1, 2, 4)),
+    4: dict(name="b96_h16_s65536_k2048_recent20", batch=96, heads=16, topk=2048,
+            seqlen=65536, structure="recent20", nsplits=(8,)),
+    5: dict(name="b64_h64_ragged_k2048_q4", batch=64, heads=64, topk=2048,
+            seqlens="cfg5", kv_seq_stride=131072, structure="ragged", q_mult=4.0,
+            nsplits=(0,)),
+}
+
+
+def config_workload(cfg: int) -> Workload:
+    c = dict(CONFIGS[cfg])
+    if c.get("seqlens") == "cfg5":
+        c["seqlens"] = _cfg5_seqlens(cfg)
+    return make_workload(seed=cfg, **c)
+
+
+def build_host_cache(w: Workload) -> np.ndarray:
+    """Full cache uint8 [B, kv_seq_stride, 640]: selected rows placed, rest 0xFF."""
+    cache = np.full((w.batch, w.kv_seq_stride, ROW_BYTES), 0xFF, dtype=np.uint8)
+    v = w.valid
+    b_i, j_i = np.nonzero(v)
+    cache[b_i, w.idx[b_i, j_i]] = w.rows[b_i, j_i]
+    return cache
