@@ -1,0 +1,161 @@
+/*
+ * smla.h -- C ABI of the sparse MLA decode library (libsmla.so, AMD gfx950).
+ *
+ * One decode step of sparse Multi-head Latent Attention: every query token
+ * (one per sequence) attends, with all of this GPU's heads, over the latent KV
+ * rows that the sequence's top-k list selects.  Keys and values are the same
+ * 512-wide latent row: 448 "nope" columns stored as fp8 e4m3fn codes with one
+ * fp32 scale per 64-column group, and 64 "rope" columns stored as bf16.
+ * Sources: "The Moment of Compilation", section "The Context: A Kernel
+ * Optimization Campaign" (one KV read shared by all heads in a batched
+ * matrix product); "The Power-of-Two Trap", sections "The Scene", "The Scale
+ * Indexing Complication" and "Input Knowledge Required" (448 + 64 latent
+ * split, per-64-column group scales, 7 groups plus one padding slot);
+ * "The 80KB Mystery", section "The Context: Optimizing Attention on
+ * Blackwell" (split-K over the selected tokens).
+ *
+ * All entry points are host functions.  Pointers to tensors are device
+ * pointers owned by the caller; the library allocates nothing per call and
+ * never synchronises the stream, so a call can be captured in a HIP graph.
+ * Invalid host-visible arguments return an error status before anything is
+ * launched and leave all outputs untouched.  Device-resident contents
+ * (indices, sequence lengths, cache bytes) are never inspected by the host.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache row format: one token's latent row, SMLA_ROW_BYTES apart.
+ *   bytes   0..447  nope, 448 fp8 e4m3fn codes (OCP, largest finite 448)
+ *   bytes 448..479  8 fp32 group scales; slot g scales nope columns 64g..64g+63
+ *                   for g < 7; slot 7 is padding and is never read
+ *   bytes 480..607  rope, 64 bf16 values
+ *   bytes 608..639  padding, never read
+ * Dequantised row: K[i] = e4m3(code[i]) * scale[i / 64] for i < 448,
+ *                  K[448 + k] = rope[k]. */
+#define SMLA_ROW_BYTES 640
+#define SMLA_NOPE_DIM 448
+#define SMLA_ROPE_DIM 64
+#define SMLA_LATENT_DIM 512
+#define SMLA_GROUP 64
+#define SMLA_SCALE_OFFSET 448
+#define SMLA_ROPE_OFFSET 480
+
+typedef enum {
+    SMLA_OK = 0,
+    SMLA_ERR_NULL = 1,         /* a required pointer is NULL */
+    SMLA_ERR_SHAPE = 2,        /* bad batch/heads/topk/splits/stride */
+    SMLA_ERR_UNSUPPORTED = 3,  /* current device is not gfx950 */
+    SMLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
+    SMLA_ERR_HIP = 5,          /* a HIP runtime call or launch failed */
+    SMLA_ERR_ALIGN = 6,        /* a pointer violates its alignment rule */
+    SMLA_ERR_NO_DEVICE = 7     /* no HIP device is available */
+} smla_status;
+
+typedef struct {
+    int32_t batch;          /* B >= 0: query tokens, one per sequence */
+    int32_t num_heads;      /* H >= 0, multiple of 16, <= 256: this GPU's heads */
+    int32_t topk;           /* >= 0: entries in each top-k list */
+    int32_t num_splits;     /* >= 0: split-K chunks per list; 0 = library's choice */
+    int64_t kv_seq_stride;  /* >= 1: cache rows between sequence b and b + 1 */
+} smla_shape;
+
+/* Split count a call with this shape uses (num_splits == 0 resolved by the
+ * launch heuristic, larger requests clamped to the number of 32-token tiles).
+ * Returns -1 for a NULL or invalid shape. */
+int32_t smla_num_splits(const smla_shape* shape);
+
+/* Workspace bytes sparse_mla_decode needs for this shape: 0 when one split is
+ * used, otherwise room for the split partials (see sparse_mla_combine).
+ * Returns 0 for a NULL or invalid shape. */
+size_t smla_workspace_bytes(const smla_shape* shape);
+
+/*
+ * sparse_mla_decode -- one decode step.
+ *
+ *   q         bf16 [B][H][512], 16-byte aligned; columns 0..447 nope, 448..511 rope
+ *   kv_cache  bytes [B][kv_seq_stride][640] (row format above), 16-byte aligned;
+ *             row t of sequence b starts at (b * kv_seq_stride + t) * 640
+ *   topk_idx  int32 [B][topk], 4-byte aligned: cache row of each list entry.
+ *             An entry is skipped when it is < 0 or >= seqlens[b] (-1 pads
+ *             short lists); entries may come in any order; a repeated entry
+ *             is counted once per occurrence
+ *   seqlens   int32 [B], 4-byte aligned; seqlens[b] <= kv_seq_stride
+ *   scale     softmax scale applied to q . K (e.g. 1/sqrt(512))
+ *   out       bf16 [B][H][512], 16-byte aligned:
+ *             out = sum_j softmax_j(scale * q . K_j) * K_j over the kept entries;
+ *             all zeros when a list keeps no entry
+ *   lse       fp32 [B][H]: natural-log sum of exp(scale * q . K_j); -inf when a
+ *             list keeps no entry
+ *   shape     sizes, see smla_shape
+ *   workspace device memory of smla_workspace_bytes(shape) bytes, 256-byte
+ *             aligned (may be NULL when that size is 0); its contents on entry
+ *             do not matter and are overwritten
+ *   stream    hipStream_t to launch on (NULL: the default stream)
+ *
+ * When batch or num_heads is 0 the call does nothing (tensor pointers may be
+ * NULL); when topk is 0, kv_cache and topk_idx may be NULL and every output
+ * row is 0 with lse -inf.
+ *
+ * Numerical contract: q . K is accumulated in fp32 from the exact bf16 query
+ * and exact fp8/bf16 key values, with the group scales applied in fp32; the
+ * softmax weights enter the value product in fp16 (value codes exact), so
+ * group scales must be finite and below 256 and rope values below 65504 in
+ * magnitude.  NaN inputs propagate to the affected outputs.
+ */
+smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                              const int32_t* seqlens, float scale, void* out, float* lse,
+                              const smla_shape* shape, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * sparse_mla_decode_partials -- the decode kernel of sparse_mla_decode alone:
+ * every split writes its normalised partial output and log-sum-exp instead of
+ * the final result (also when the shape resolves to one split).
+ *
+ *   q, kv_cache, topk_idx, seqlens, scale, shape: as for sparse_mla_decode
+ *   o_part    fp32 [B][H][S][512], 16-byte aligned, S = smla_num_splits(shape);
+ *             split i covers list entries [i*C, min((i+1)*C, topk)) with
+ *             C = smla_split_size(shape); an empty split writes 0
+ *   lse_part  fp32 [B][H][S]: the split's log-sum-exp, -inf when it keeps no entry
+ * sparse_mla_combine(o_part, lse_part, ...) then yields sparse_mla_decode's
+ * result.
+ */
+smla_status sparse_mla_decode_partials(const void* q, const void* kv_cache,
+                                       const int32_t* topk_idx, const int32_t* seqlens,
+                                       float scale, const smla_shape* shape, float* o_part,
+                                       float* lse_part, void* stream);
+
+/* List entries per split (C above, a multiple of 32); -1 for an invalid shape. */
+int32_t smla_split_size(const smla_shape* shape);
+
+/*
+ * sparse_mla_combine -- the log-sum-exp merge of split partials (the second
+ * kernel of sparse_mla_decode, exposed on its own).
+ *
+ *   o_part    fp32 [B][H][num_splits][512]: each split's normalised output
+ *   lse_part  fp32 [B][H][num_splits]: each split's log-sum-exp (-inf = empty)
+ *   out       bf16 [B][H][512]: sum_i exp(lse_i - LSE) * o_part_i
+ *   lse       fp32 [B][H]: LSE = log(sum_i exp(lse_i)); -inf and out = 0 when
+ *             every split is empty
+ * o_part and out must be 16-byte aligned.  sparse_mla_decode places o_part at
+ * offset 0 of its workspace and lse_part right after it.
+ */
+smla_status sparse_mla_combine(const float* o_part, const float* lse_part, int32_t batch,
+                               int32_t num_heads, int32_t num_splits, void* out, float* lse,
+                               void* stream);
+
+/* Static description of a status code. */
+const char* smla_status_str(smla_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

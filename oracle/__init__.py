@@ -112,20 +112,21 @@ def decode(w, cache=None, **kw):
     return out, lse
 
 
-def split_bounds(topk: int, nsplit: int):
-    """Contiguous chunks of the list: split i covers [i*c, min((i+1)*c, topk))."""
-    c = -(-topk // nsplit) if topk else 0
+def split_bounds(topk: int, nsplit: int, chunk: int | None = None):
+    """Contiguous chunks of the list: split i covers [i*c, min((i+1)*c, topk)),
+    c = ceil(topk / nsplit) unless given."""
+    c = chunk if chunk is not None else (-(-topk // nsplit) if topk else 0)
     return [(min(i * c, topk), min((i + 1) * c, topk)) for i in range(nsplit)]
 
 
-def decode_splits(w, nsplit, cache=None):
+def decode_splits(w, nsplit, cache=None, chunk=None):
     """Per-split partial results: o fp64 [B,H,S,512] (normalised), lse fp64 [B,H,S]."""
     if cache is None:
         from workloads import build_host_cache
         cache = build_host_cache(w)
     o = np.zeros((w.batch, w.heads, nsplit, 512))
     l = np.zeros((w.batch, w.heads, nsplit))
-    for i, (lo, hi) in enumerate(split_bounds(w.topk, nsplit)):
+    for i, (lo, hi) in enumerate(split_bounds(w.topk, nsplit, chunk)):
         oi, li, _ = decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads,
                                w.scale, idx_offset=lo, idx_cols=hi - lo)
         o[:, :, i] = oi

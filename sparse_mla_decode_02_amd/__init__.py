@@ -1,0 +1,159 @@
+"""Python binding of libsmla.so (sparse MLA decode on AMD gfx950).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels
+of libsmla.so.  Tensors are torch tensors on the GPU (torch provides device
+memory and streams); the functions pass their data pointers and the current
+HIP stream through the C ABI declared in include/smla.h.  If the library has
+not been built, importing works but every call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsmla.so")
+
+SMLA_OK = 0
+ROW_BYTES = 640
+LATENT = 512
+NOPE = 448
+ROPE = 64
+
+STATUS_NAMES = {
+    0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_UNSUPPORTED",
+    4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_HIP", 6: "SMLA_ERR_ALIGN", 7: "SMLA_ERR_NO_DEVICE",
+}
+
+EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine",
+           "smla_workspace_bytes", "smla_num_splits", "smla_split_size", "smla_status_str")
+
+
+class SmlaShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("kv_seq_stride", ctypes.c_int64)]
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsmla.so (built by build.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library missing: {LIB_PATH} (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        shp = ctypes.POINTER(SmlaShape)
+        L.smla_num_splits.argtypes = [shp]
+        L.smla_num_splits.restype = i32
+        L.smla_split_size.argtypes = [shp]
+        L.smla_split_size.restype = i32
+        L.sparse_mla_decode_partials.argtypes = [vp, vp, vp, vp, f32, shp, vp, vp, vp]
+        L.sparse_mla_decode_partials.restype = ctypes.c_int
+        L.smla_workspace_bytes.argtypes = [shp]
+        L.smla_workspace_bytes.restype = ctypes.c_size_t
+        L.smla_status_str.argtypes = [ctypes.c_int]
+        L.smla_status_str.restype = ctypes.c_char_p
+        L.sparse_mla_decode.argtypes = [vp, vp, vp, vp, f32, vp, vp, shp, vp, ctypes.c_size_t, vp]
+        L.sparse_mla_decode.restype = ctypes.c_int
+        L.sparse_mla_combine.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+        L.sparse_mla_combine.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().smla_status_str(status).decode()
+
+
+def _check(status: int):
+    if status != SMLA_OK:
+        raise SmlaError(status, status_str(status))
+
+
+def make_shape(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> SmlaShape:
+    return SmlaShape(int(batch), int(num_heads), int(topk), int(num_splits), int(kv_seq_stride))
+
+
+def num_splits(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> int:
+    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride)
+    return int(lib().smla_num_splits(ctypes.byref(s)))
+
+
+def split_size(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> int:
+    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride)
+    return int(lib().smla_split_size(ctypes.byref(s)))
+
+
+def workspace_bytes(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> int:
+    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride)
+    return int(lib().smla_workspace_bytes(ctypes.byref(s)))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def sparse_mla_decode(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, num_splits=0,
+                      kv_seq_stride=None, workspace=None, stream=None):
+    """One decode step through libsmla.so.
+
+    q: bf16 [B,H,512]; kv_cache: uint8 [B, kv_seq_stride, 640] (or flat);
+    topk_idx: int32 [B,topk]; seqlens: int32 [B]; out: bf16 [B,H,512];
+    lse: float32 [B,H]; workspace: uint8 device tensor of at least
+    workspace_bytes(...) bytes, allocated here when None.
+    """
+    import torch
+    B, H, _ = q.shape
+    topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    if kv_seq_stride is None:
+        kv_seq_stride = kv_cache.shape[1] if kv_cache.dim() == 3 else kv_cache.numel() // (max(B, 1) * ROW_BYTES)
+    shape = make_shape(B, H, topk, num_splits, kv_seq_stride)
+    L = lib()
+    need = int(L.smla_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.sparse_mla_decode(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(seqlens),
+                               ctypes.c_float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape),
+                               _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream)))
+    return out, lse
+
+
+def sparse_mla_decode_partials(q, kv_cache, topk_idx, seqlens, scale, o_part, lse_part, *,
+                               num_splits=0, kv_seq_stride=None, stream=None):
+    """Decode kernel only: per-split partials o_part fp32 [B,H,S,512], lse_part fp32 [B,H,S]."""
+    B, H, _ = q.shape
+    topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    if kv_seq_stride is None:
+        kv_seq_stride = kv_cache.shape[1]
+    shape = make_shape(B, H, topk, num_splits, kv_seq_stride)
+    _check(lib().sparse_mla_decode_partials(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(seqlens),
+                                            ctypes.c_float(scale), ctypes.byref(shape), _ptr(o_part),
+                                            _ptr(lse_part), _stream_handle(stream)))
+    return o_part, lse_part
+
+
+def sparse_mla_combine(o_part, lse_part, out, lse, *, stream=None):
+    """Merge split partials o_part fp32 [B,H,S,512], lse_part fp32 [B,H,S]."""
+    B, H, S, _ = o_part.shape
+    _check(lib().sparse_mla_combine(_ptr(o_part), _ptr(lse_part), B, H, S, _ptr(out), _ptr(lse),
+                                    _stream_handle(stream)))
+    return out, lse

@@ -1,0 +1,120 @@
+"""The C ABI of libsmla.so on a machine without a GPU: the library loads,
+exports every function include/smla.h declares, and rejects bad host-visible
+arguments with the documented status before touching any device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mla_decode_02_amd as smla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(smla.LIB_PATH), reason="libsmla.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_\w+|sparse_mla_\w+)\s*\(", text)))
+
+
+@needs_lib
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(smla.EXPORTS)
+    L = ctypes.CDLL(smla.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@needs_lib
+def test_status_strings():
+    for code in range(8):
+        s = smla.status_str(code)
+        assert isinstance(s, str) and s
+    assert smla.status_str(0) == "ok"
+    assert smla.status_str(99) == "unknown status"
+
+
+@needs_lib
+def test_split_resolution_and_workspace_size():
+    # one split: no workspace
+    assert smla.num_splits(1, 16, 64, num_splits=1) == 1
+    assert smla.workspace_bytes(1, 16, 64, num_splits=1) == 0
+    # requests are clamped to the number of 32-entry tiles
+    assert smla.num_splits(1, 16, 64, num_splits=8) == 2
+    assert smla.num_splits(4, 16, 512, num_splits=4) == 4
+    assert smla.num_splits(96, 16, 2048, num_splits=8) == 8
+    # workspace: fp32 partials [B,H,S,512] then lse [B,H,S], each 256-byte rounded
+    rows = 96 * 16 * 8
+    exp = ((rows * 512 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert smla.workspace_bytes(96, 16, 2048, num_splits=8) == exp
+    # heuristic always returns a usable count
+    for B, H, k in [(1, 16, 64), (32, 64, 512), (64, 64, 2048), (0, 16, 8), (3, 48, 45), (2, 128, 0)]:
+        n = smla.num_splits(B, H, k)
+        assert n >= 1
+        assert n <= max(1, -(-k // 32))
+    # invalid shapes
+    assert smla.num_splits(1, 15, 64) == -1
+    assert smla.num_splits(1, 16, -1) == -1
+    assert smla.num_splits(-1, 16, 64) == -1
+    assert smla.num_splits(1, 16, 64, kv_seq_stride=0) == -1
+    assert smla.workspace_bytes(1, 15, 64) == 0
+
+
+def _call(L, shape, ptrs=None, ws=None, wsb=0):
+    p = ptrs or {}
+    fake = ctypes.c_void_p(1 << 20)   # host-side non-null, aligned; never dereferenced
+    args = [p.get(n, fake) for n in ("q", "kv", "idx", "seqlens")]
+    return L.sparse_mla_decode(*args, ctypes.c_float(0.05), p.get("out", fake), p.get("lse", fake),
+                               ctypes.byref(shape) if shape is not None else None,
+                               ws, ctypes.c_size_t(wsb), None)
+
+
+@needs_lib
+def test_argument_errors_before_any_device_work():
+    L = smla.lib()
+    good = smla.make_shape(2, 16, 64, 1, 128)
+    assert _call(L, None) == 1                                   # NULL shape
+    for n in ("q", "kv", "idx", "seqlens", "out", "lse"):
+        assert _call(L, good, {n: None}) == 1, n                  # NULL operand
+    assert _call(L, smla.make_shape(2, 20, 64, 1, 128)) == 2      # H not a multiple of 16
+    assert _call(L, smla.make_shape(2, 272, 64, 1, 128)) == 2     # H too large
+    assert _call(L, smla.make_shape(2, 16, -3, 1, 128)) == 2      # negative topk
+    assert _call(L, smla.make_shape(-1, 16, 64, 1, 128)) == 2     # negative batch
+    assert _call(L, smla.make_shape(2, 16, 64, -2, 128)) == 2     # negative splits
+    assert _call(L, smla.make_shape(2, 16, 64, 1, 0)) == 2        # stride < 1
+    assert _call(L, good, {"q": ctypes.c_void_p((1 << 20) + 4)}) == 6   # q misaligned
+    assert _call(L, good, {"idx": ctypes.c_void_p((1 << 20) + 2)}) == 6  # idx misaligned
+    split = smla.make_shape(2, 16, 64, 2, 128)
+    need = L.smla_workspace_bytes(ctypes.byref(split))
+    assert need > 0
+    assert _call(L, split) == 4                                   # workspace missing
+    assert _call(L, split, ws=ctypes.c_void_p(1 << 21), wsb=need - 1) == 4
+    assert _call(L, split, ws=ctypes.c_void_p((1 << 21) + 16), wsb=need) == 6
+
+
+@needs_lib
+def test_valid_call_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = smla.lib()
+    assert _call(L, smla.make_shape(2, 16, 64, 1, 128)) == 7
+    assert L.sparse_mla_combine(ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), 1, 16, 2,
+                                ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None) == 7
+    assert L.sparse_mla_combine(None, ctypes.c_void_p(1 << 20), 1, 16, 2,
+                                ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None) == 1
+    assert L.sparse_mla_combine(ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), 1, 16, 0,
+                                ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None) == 2
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(smla, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(smla, "_lib", None)
+    with pytest.raises(RuntimeError, match="HIP library missing"):
+        smla.lib()

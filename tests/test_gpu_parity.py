@@ -1,0 +1,193 @@
+"""GPU parity: libsmla.so (through its C ABI) against the fp64 CPU oracle on
+the same seeded inputs.  Marked ``gpu``."""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mla_decode_02_amd as smla
+from tests._gpu import compare, device_inputs, log, run_decode
+from workloads import build_host_cache, config_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=2)
+def cfg_case(n):
+    log(f"building workload config {n}")
+    w = config_workload(n)
+    cache = build_host_cache(w)
+    out, lse, used = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens,
+                                       w.heads, w.scale)
+    del cache
+    log(f"oracle config {n}: {used} threads")
+    return w, out, lse
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    cfg_case.cache_clear()
+
+
+def case_small(seed, **kw):
+    w = make_workload(seed=seed, **kw)
+    cache = build_host_cache(w)
+    out, lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads, w.scale)
+    return w, out, lse
+
+
+CFG_SPLITS = [(1, 1), (1, 2), (1, 0), (2, 4), (2, 0), (3, 1), (3, 2), (3, 4), (3, 0),
+              (4, 8), (4, 0), (5, 0), (5, 3), (5, 1)]
+
+
+@pytest.mark.parametrize("cfg,nsplit", CFG_SPLITS)
+def test_config_parity(cfg, nsplit):
+    log(f"case: config {cfg} num_splits {nsplit}")
+    w, ref_out, ref_lse = cfg_case(cfg)
+    out, lse = run_decode(w, num_splits=nsplit)
+    compare(out, lse, ref_out, ref_lse, label=f"cfg{cfg}/ns{nsplit}->{smla.num_splits(w.batch, w.heads, w.topk, nsplit)}")
+
+
+@pytest.mark.parametrize("heads", [16, 32, 48, 64, 128])
+@pytest.mark.parametrize("topk,nsplit", [(45, 1), (45, 2), (100, 0), (1, 1)])
+def test_head_counts_and_ragged_lists(heads, topk, nsplit):
+    log(f"case: heads {heads} topk {topk} nsplit {nsplit}")
+    w, ref_out, ref_lse = case_small(100 + heads + topk, batch=3, heads=heads, topk=topk,
+                                     seqlens=[300, 50, 7], kv_seq_stride=300, structure="ragged",
+                                     q_mult=2.0)
+    out, lse = run_decode(w, num_splits=nsplit)
+    compare(out, lse, ref_out, ref_lse, label=f"H{heads}/k{topk}/ns{nsplit}")
+
+
+def test_masked_entries_anywhere_and_out_of_range():
+    w = make_workload(seed=7, batch=4, heads=64, topk=128, seqlen=1000)
+    rng = np.random.default_rng(7)
+    pos = rng.random(w.idx.shape) < 0.3
+    w.idx[pos] = -1
+    w.idx[rng.random(w.idx.shape) < 0.05] = 1000 + 5     # beyond seqlen (and past the rows)
+    w.idx[0, :] = -1                                      # one list with nothing kept
+    cache = build_host_cache(w)
+    ref_out, ref_lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads, w.scale)
+    for ns in (1, 2, 4):
+        out, lse = run_decode(w, num_splits=ns)
+        compare(out, lse, ref_out, ref_lse, label=f"masked/ns{ns}")
+        assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+def test_order_of_list_does_not_matter():
+    w, ref_out, ref_lse = case_small(8, batch=2, heads=64, topk=256, seqlen=4096, q_mult=4.0)
+    inputs = device_inputs(w)
+    out1, lse1 = run_decode(w, inputs, num_splits=2)
+    srt = torch.from_numpy(np.sort(w.idx, axis=1)).to("cuda:0")
+    out2, lse2 = run_decode(w, inputs, num_splits=2, idx=srt)
+    compare(out1, lse1, ref_out, ref_lse, label="shuffled")
+    compare(out2, lse2, ref_out, ref_lse, label="sorted")
+
+
+def test_deterministic_across_runs():
+    w, _, _ = case_small(9, batch=8, heads=64, topk=512, seqlen=8192)
+    inputs = device_inputs(w)
+    a = run_decode(w, inputs, num_splits=4)
+    b = run_decode(w, inputs, num_splits=4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_single_token_returns_row_exactly():
+    # one kept entry with unit scales: out is the row itself in bf16 (fp8 codes
+    # are exact in bf16; the device fp8 decode sees every non-NaN code)
+    w = make_workload(seed=10, batch=1, heads=16, topk=8, seqlen=4)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    row = w.rows[0, 0].copy()
+    row[:448] = np.resize(codes, 448)
+    row[448:476] = np.ones(7, dtype=np.float32).view(np.uint8)
+    w.rows[0, :] = row
+    w.idx[0] = [2, -1, -1, -1, -1, -1, -1, -1]
+    w.q_bits[:] = 0
+    cache = build_host_cache(w)
+    ref_out, ref_lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads, w.scale)
+    for ns in (1, 2):
+        out, lse = run_decode(w, num_splits=ns)
+        assert np.array_equal(out, ref_out), ns      # exact: every value is a bf16 number
+        assert np.all(lse == 0.0)
+
+
+def test_device_fp8_decode_in_logits():
+    # q = e_i selects one nope column: lse = scale * e4m3(code_i) (single kept row)
+    w = make_workload(seed=12, batch=16, heads=16, topk=1, seqlen=1)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    row = w.rows[0, 0].copy()
+    row[:448] = np.resize(codes, 448)
+    row[448:476] = np.ones(7, dtype=np.float32).view(np.uint8)
+    w.rows[:, 0] = row
+    w.idx[:] = 0
+    q = np.zeros((16, 16, 512), dtype=np.uint16)
+    cols = np.arange(256).reshape(16, 16) % 448
+    for b in range(16):
+        for h in range(16):
+            q[b, h, cols[b, h]] = 0x3F80     # bf16 1.0
+    w.q_bits = q
+    out, lse = run_decode(w, num_splits=1)
+    expect = np.array([[w.scale * oracle.e4m3fn_value(row[cols[b, h]]) for h in range(16)] for b in range(16)])
+    assert np.allclose(lse, expect, rtol=1e-6, atol=1e-7)
+
+
+def test_empty_batch_and_empty_lists():
+    w = make_workload(seed=13, batch=2, heads=16, topk=0, seqlen=10)
+    out, lse = run_decode(w, num_splits=0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    w0 = make_workload(seed=14, batch=0, heads=16, topk=8, seqlen=10)
+    q = torch.zeros((0, 16, 512), dtype=torch.bfloat16, device="cuda:0")
+    out0 = torch.zeros((0, 16, 512), dtype=torch.bfloat16, device="cuda:0")
+    smla.sparse_mla_decode(q, torch.zeros((0, 10, 640), dtype=torch.uint8, device="cuda:0"),
+                           torch.zeros((0, 8), dtype=torch.int32, device="cuda:0"),
+                           torch.zeros((0,), dtype=torch.int32, device="cuda:0"), w0.scale, out0,
+                           torch.zeros((0, 16), device="cuda:0"), kv_seq_stride=10)
+    torch.cuda.synchronize()
+
+
+def test_combine_kernel_against_oracle_combine():
+    # partials from the oracle (including empty splits) merged by the GPU combine
+    w = make_workload(seed=15, batch=3, heads=32, topk=96, seqlens=[40, 500, 2], structure="ragged",
+                      kv_seq_stride=500, q_mult=4.0)
+    cache = build_host_cache(w)
+    o_p, l_p = oracle.decode_splits(w, 5, cache)
+    ref_out, ref_lse = oracle.combine(o_p, l_p)
+    o_dev = torch.from_numpy(o_p.astype(np.float32)).to("cuda:0")
+    l_dev = torch.from_numpy(l_p.astype(np.float32)).to("cuda:0")
+    out = torch.empty((3, 32, 512), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((3, 32), dtype=torch.float32, device="cuda:0")
+    smla.sparse_mla_combine(o_dev, l_dev, out, lse)
+    torch.cuda.synchronize()
+    compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            ref_out, ref_lse, label="combine")
+
+
+@pytest.mark.parametrize("topk,nsplit", [(512, 4), (200, 3), (96, 8)])
+def test_split_partials_against_oracle_partials(topk, nsplit):
+    # the decode kernel alone: each split's normalised output and lse
+    w = make_workload(seed=16, batch=4, heads=64, topk=topk, seqlens=[3000, 150, 20, 3000],
+                      kv_seq_stride=3000, structure="ragged", q_mult=4.0)
+    S = smla.num_splits(w.batch, w.heads, w.topk, nsplit, w.kv_seq_stride)
+    C = smla.split_size(w.batch, w.heads, w.topk, nsplit, w.kv_seq_stride)
+    cache = build_host_cache(w)
+    ref_o, ref_l = oracle.decode_splits(w, S, cache, chunk=C)
+    q, cache_d, idx, seqlens = device_inputs(w)
+    o = torch.full((4, 64, S, 512), float("nan"), device="cuda:0")
+    l = torch.full((4, 64, S), float("nan"), device="cuda:0")
+    smla.sparse_mla_decode_partials(q, cache_d, idx, seqlens, w.scale, o, l, num_splits=nsplit)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy().astype(np.float64)
+    l = l.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all()
+    assert np.array_equal(np.isneginf(l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.abs(l[fin] - ref_l[fin]).max() <= 1e-3
+    err = np.abs(o - ref_o)
+    assert err.max() <= 1e-2 * max(1.0, np.abs(ref_o).max() / 4), err.max()
+    assert np.linalg.norm(o - ref_o) / np.linalg.norm(ref_o) <= 5e-3
