@@ -45,9 +45,6 @@ constexpr int kRowBytes = SMLA_ROW_BYTES;   // 640
 constexpr int kNope = SMLA_NOPE_DIM;        // 448
 constexpr int kLatent = SMLA_LATENT_DIM;    // 512
 constexpr int kTile = 32;                   // tokens per tile
-constexpr int kChunks = 38;                 // 16-byte pieces of a row that are read (0..607)
-constexpr int kKrStride = 624;              // LDS bytes per token row (608 + 16 pad)
-constexpr int kRopeStride = 144;            // LDS bytes per token of the fp16 rope copy
 constexpr float kTau = 8.0f;                // lazy-rescale threshold (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -65,12 +62,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-struct __attribute__((aligned(16))) TileLds {
-    uint8_t kr[kTile * kKrStride];       // raw row bytes 0..607 of each token
-    uint8_t ropeh[kTile * kRopeStride];  // rope as fp16, 64 values per token
-    float sq[8][kTile];                  // logit factor per (group, token): scale_g * c (rope: c)
-    float sv[8][kTile];                  // value factor per (group, token): scale_g (rope: 1)
-};
+constexpr int kPieces = 39;                  // 16-byte pieces staged per row (608 payload + pad)
+constexpr int kRowLds = kPieces * 16;        // 624 bytes per token row in LDS
+constexpr int kTileBlocks = (kTile * kPieces + 63) / 64;   // 1 KB blocks per tile (20)
+constexpr int kMaxChunk = 2048;              // list entries per workgroup (index chunk in LDS)
+
+// A zero row: masked list entries are gathered from here, so every staged byte
+// is finite and a masked token contributes exactly zero.
+__device__ __attribute__((aligned(256))) uint8_t g_zero_row[kRowBytes];
 
 __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -94,24 +93,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return r;
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
-    return __uint_as_float(bits16 << 16);
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-    _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    uint16_t ua, ub;
-    memcpy(&ua, &ha, 2);
-    memcpy(&ub, &hb, 2);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
-    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-    // round to nearest even; NaN stays NaN (quiet bit set)
-    uint32_t ra = (ua & 0x7fffffffu) > 0x7f800000u ? (ua | 0x00400000u) : ua + 0x7fffu + ((ua >> 16) & 1u);
-    uint32_t rb = (ub & 0x7fffffffu) > 0x7f800000u ? (ub | 0x00400000u) : ub + 0x7fffu + ((ub >> 16) & 1u);
-    return (ra >> 16) | (rb & 0xffff0000u);
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32: round to nearest even
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    return u;
 }
 
 // Token held in MFMA k-slot `slot` (0..31) of a 32-token tile.  The S^T
@@ -120,6 +106,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
 __device__ __forceinline__ int slot_token(int slot) {
     int q = slot >> 3, r = slot & 7;
     return r < 4 ? 4 * q + r : 16 + 4 * q + (r - 4);
+}
+
+// 16-byte gather of one lane straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4; the LDS base goes through M0 and must be
+// wave-uniform).  Written as inline assembly so that the compiler does not
+// treat every later LDS read as dependent on every gather in flight; the
+// ordering is explicit instead: wait_vmcnt<N>() then lds_barrier().
+__device__ __forceinline__ void gather16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+
+// Workgroup barrier without a memory fence: only this wave's LDS operations are
+// waited for, so gathers still in flight into other ring slots stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 struct DecodeArgs {
@@ -135,250 +148,363 @@ struct DecodeArgs {
     float logit_factor;   // scale * log2(e)
     int32_t batch, heads, topk, nsplit, chunk, n_hg;
     int32_t force_partials;   // write split partials even when nsplit == 1
+    int32_t xcd_remap;        // grid is a multiple of 8: keep a sequence's blocks on one XCD
 };
 
-// One workgroup = (sequence b, head group hg, split s); NW waves, 16 heads each.
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void smla_decode_kernel(DecodeArgs a) {
-    constexpr int NT = 64 * NW;
-    constexpr int KPER = (kTile * kChunks + NT - 1) / NT;   // 16-byte pieces per thread per tile
-    __shared__ TileLds lds;
+// One 32-token tile for one wave: 16 heads x one latent half (DH = 0: nope
+// groups 0..3; DH = 1: nope groups 4..6 and the rope).  st is the tile's ring
+// slot (32 raw rows, kRowLds apart); vmask marks the kept tokens.  The partial
+// logits of the two halves are exchanged through xs_mine / xs_other, and the
+// caller's workgroup barrier separates the write from the partner's read.
+template <int DH>
+__device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, const bf16x8 (&qop)[8],
+                                             f32x4 (&acc_o)[16], float& m_run, float& l_run,
+                                             float* sT, float* xs_mine, const float* xs_other,
+                                             int lane, float logit_factor) {
+    constexpr int G0 = 4 * DH;           // first nope group
+    constexpr int NG = DH == 0 ? 4 : 3;  // nope groups
+    const int qg = lane >> 4, ln = lane & 15;
+
+    // group scales of this half, transposed to [group][token] in this wave's
+    // own LDS block (a wave's LDS operations complete in order)
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        const int e = lane + 64 * k;          // 0..127: token e / 4, group G0 + e % 4
+        const int t = e >> 2, g = e & 3;
+        if (g < NG) sT[g * kTile + t] = *(const float*)(st + t * kRowLds + SMLA_SCALE_OFFSET + 4 * (G0 + g));
+    }
+
+    // ---------------- partial S^T over this half's columns, per 16-token half:
+    // operands read first, then one MFMA chain per group (independent chains)
+    f32x4 s[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+        const uint8_t* krow = st + (16 * tt + ln) * kRowLds;
+        u32x4 raw[NG];
+        u32x4 rrope[2];
+#pragma unroll
+        for (int g = 0; g < NG; g++) raw[g] = *(const u32x4*)(krow + 64 * (G0 + g) + 16 * qg);
+        if (DH == 1) {
+            rrope[0] = *(const u32x4*)(krow + SMLA_ROPE_OFFSET + 32 * qg);
+            rrope[1] = *(const u32x4*)(krow + SMLA_ROPE_OFFSET + 16 + 32 * qg);
+        }
+        f32x4 acc[NG + 1];
+#pragma unroll
+        for (int g = 0; g < NG; g++)
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][0], raw[g][1]), qop[2 * g],
+                                                             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        if (DH == 1)
+            acc[NG] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rrope[0]), qop[6],
+                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; g++)
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][2], raw[g][3]), qop[2 * g + 1],
+                                                             acc[g], 0, 0, 0);
+        if (DH == 1)
+            acc[NG] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rrope[1]), qop[7], acc[NG], 0, 0, 0);
+        f32x4 v = DH == 1 ? acc[NG] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < NG; g++) v += *(const f32x4*)(sT + g * kTile + 16 * tt + 4 * qg) * acc[g];
+        s[tt] = v;
+    }
+
+    // exchange with the partner wave; both form S = S_half0 + S_half1 in the
+    // same order, so both hold bit-identical logits
+    *(f32x4*)(xs_mine + 8 * lane) = s[0];
+    *(f32x4*)(xs_mine + 8 * lane + 4) = s[1];
+    lds_barrier();
+    {
+        const f32x4 o0 = *(const f32x4*)(xs_other + 8 * lane);
+        const f32x4 o1 = *(const f32x4*)(xs_other + 8 * lane + 4);
+        s[0] = DH == 0 ? s[0] + o0 : o0 + s[0];
+        s[1] = DH == 0 ? s[1] + o1 : o1 + s[1];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float z = s[tt][j] * logit_factor;
+            s[tt][j] = ((vmask >> (16 * tt + 4 * qg + j)) & 1) ? z : -INFINITY;
+        }
+
+    // ---------------- online softmax (log2 domain), lazy rescale
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > m_run + kTau;
+    if (__any(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc_o[i] *= alpha;
+    }
+    const float base = m_run == -INFINITY ? 0.f : m_run;
+    float p[8];   // k-slot order: tokens 4q+j (j < 4), then 16+4q+(j-4)
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        p[j] = __builtin_amdgcn_exp2f(s[j >> 2][j & 3] - base);
+        l_run += p[j];
+    }
+
+    // ---------------- O^T += V^T . P^T over this half's columns
+    // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2), byte half j%2
+    const uint8_t* tr_row = st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1);
+    s16x4 rv[4][2];
+    if (DH == 1) {
+        // rope V^T via tr16: lane 16q + 4r + c supplies slot_token(8q + r), then (8q + 4 + r)
+        const int col = 8 * (ln & 3);
+        const uint8_t* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + SMLA_ROPE_OFFSET + col;
+        const uint8_t* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + SMLA_ROPE_OFFSET + col;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            rv[dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
+            rv[dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; g++) {
+        i32x2 vraw[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+            vraw[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * (G0 + g) + 16 * dt));
+        const f32x4 sv0 = *(const f32x4*)(sT + g * kTile + 4 * qg);
+        const f32x4 sv1 = *(const f32x4*)(sT + g * kTile + 16 + 4 * qg);
+        // weights fp16(p * scale_g); exact fp8 -> fp16 value codes
+        f16x8 bop;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            bop[j] = (_Float16)(p[j] * sv0[j]);
+            bop[4 + j] = (_Float16)(p[4 + j] * sv1[j]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+            acc_o[4 * g + dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                codes_to_f16((uint32_t)vraw[dt][0], (uint32_t)vraw[dt][1]), bop, acc_o[4 * g + dt], 0, 0, 0);
+    }
+    if (DH == 1) {
+        // rope: bf16 values as stored; weights split into bf16 high and low parts
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const __bf16 h = (__bf16)p[j];
+            phi[j] = h;
+            plo[j] = (__bf16)(p[j] - (float)h);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            bf16x8 aop;
+            memcpy(&aop, rv[dt], 16);
+            f32x4 c = acc_o[12 + dt];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, c, 0, 0, 0);
+            acc_o[12 + dt] = c;
+        }
+    }
+}
+
+// Workgroup geometry.  A workgroup covers NHG groups of 16 heads.  Each head
+// group is served by a pair of waves, one per latent half: half 0 holds nope
+// groups 0..3 (columns 0..255), half 1 holds nope groups 4..6 and the rope
+// (columns 256..511).  TW such sets of pairs take different tiles of the list
+// (token-parallel) and are merged at the end.  Each wave thus holds half of
+// its heads' query (32 registers) and half of their output accumulator (64
+// registers), which lets two waves share a SIMD.
+template <int NHG, int TW>
+struct Geo {
+    static constexpr int NWAVES = NHG * 2 * TW;
+    static constexpr int NT = 64 * NWAVES;
+    static constexpr int STAGE = kTileBlocks * 1024;              // one tile of raw rows
+    static constexpr int NS = TW == 1 ? 5 : 6;                    // ring stages
+    static constexpr int PMAX = (kTileBlocks + NWAVES - 1) / NWAVES;   // loads per wave per tile
+    static constexpr int XS = NWAVES * 64 * 8 * 4;                // partial-logit exchange
+    static constexpr int ST = NWAVES * 4 * kTile * 4;             // per-wave transposed scales
+};
+
+// One workgroup = (sequence b, head block hb, split s).  Rows of the split's
+// list are gathered straight into an LDS ring of NS tiles (global_load_lds,
+// 16 bytes per lane), NS - TW tiles in flight while TW tiles are computed.
+template <int NHG, int TW>
+__global__ __launch_bounds__(64 * NHG * 2 * TW, 2) void smla_decode_kernel(DecodeArgs a) {
+    using G = Geo<NHG, TW>;
+    constexpr int NWAVES = G::NWAVES, NT = G::NT, STAGE = G::STAGE, NS = G::NS;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
+    __shared__ int32_t idx_s[kMaxChunk + TW * kTile];   // padded to whole rounds
+    __shared__ __attribute__((aligned(16))) float xs[NWAVES][64 * 8];
+    __shared__ __attribute__((aligned(16))) float sts[NWAVES][4 * kTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int qg = lane >> 4;      // lane group 0..3
-    const int ln = lane & 15;      // column within the 16x16 tile (head)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int dh = wave & 1;                   // latent half
+    const int hw = (wave >> 1) % NHG;          // head group within the block
+    const int tw = (wave >> 1) / NHG;          // token-parallel set
+    const int partner = wave ^ 1;
+    const int qg = lane >> 4;                  // lane group 0..3
+    const int ln = lane & 15;                  // head column of the 16x16 tiles
+    const int g0 = 4 * dh;                     // first nope group of this half
+    const int ng = dh == 0 ? 4 : 3;            // nope groups of this half
 
     int bid = blockIdx.x;
-    const int hg = bid % a.n_hg;
+    if (a.xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+    const int hb = bid % a.n_hg;
     bid /= a.n_hg;
     const int split = bid % a.nsplit;
     const int b = bid / a.nsplit;
 
-    const int head = hg * (16 * NW) + 16 * wave + ln;
+    const int head = hb * (16 * NHG) + 16 * hw + ln;
     const int t_begin = split * a.chunk;
     const int t_end = min(a.topk, t_begin + a.chunk);
-    const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
+    const int n_ent = max(t_end - t_begin, 0);
+    const int ntiles = (n_ent + kTile - 1) / kTile;
+    const int nrounds = (ntiles + TW - 1) / TW;
     const int seqlen = a.seqlens[b];
-    const int32_t* idx_b = a.idx + (int64_t)b * a.topk;
     const uint8_t* kv_b = a.kv + (int64_t)b * a.kv_seq_stride * kRowBytes;
 
-    // ---- query as the B operand of S^T = K . Q^T (k-slot order matches the K reads)
-    bf16x8 qn[7][2], qr[2];
+    // ---- index chunk -> LDS: the cache row of each entry, or -1 when masked
     {
-        const uint16_t* qh = a.q + ((int64_t)b * a.heads + head) * kLatent;
+        const int32_t* src = a.idx + (int64_t)b * a.topk + t_begin;
+        for (int i = tid; i < nrounds * TW * kTile; i += NT) {
+            int row = -1;
+            if (i < n_ent) {
+                row = src[i];
+                if (row < 0 || row >= seqlen) row = -1;
+            }
+            idx_s[i] = row;
+        }
+    }
+    // ---- this half of the query as the B operand of S^T = K . Q^T
+    // (k-slot order matches the K reads: lane group q takes columns 16q..16q+15
+    // of every 64-column group, 8 per K-step)
+    bf16x8 qop[8];
+    {
+        const uint16_t* qh = a.q + ((int64_t)b * a.heads + head) * kLatent + 256 * dh;
 #pragma unroll
-        for (int g = 0; g < 7; g++)
+        for (int g = 0; g < 4; g++)
 #pragma unroll
             for (int ks = 0; ks < 2; ks++)
-                qn[g][ks] = as_bf16x8(*(const u32x4*)(qh + 64 * g + 16 * qg + 8 * ks));
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++)
-            qr[ks] = as_bf16x8(*(const u32x4*)(qh + kNope + 16 * qg + 8 * ks));
+                qop[2 * g + ks] = as_bf16x8(*(const u32x4*)(qh + 64 * g + 16 * qg + 8 * ks));
     }
+    wait_vmcnt<0>();
+    __syncthreads();
 
-    f32x4 acc_o[32];
+    // ---- gather of tile t into ring slot t % NS.  The tile is 1248 16-byte
+    // pieces (32 rows x 39); piece c is row c/39, piece c%39, placed at byte 16c
+    // of the slot.  1 KB block k of the slot is loaded by wave k % NWAVES.
+    // Pieces past the tile and tiles past the end load the zero row, so each
+    // wave issues the same number of loads for every tile.
+    auto issue = [&](int t) {
+        uint8_t* base = ring + (t % NS) * STAGE;
 #pragma unroll
-    for (int i = 0; i < 32; i++) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;   // base of the exponentials for this lane's head
+        for (int k = 0; k < G::PMAX; k++) {
+            const int blk = k * NWAVES + wave;
+            if (blk < kTileBlocks) {
+                const int c = blk * 64 + lane;
+                const int r = c / kPieces;
+                const int p = c - r * kPieces;
+                const uint8_t* src = g_zero_row;
+                if (t < ntiles && c < kTile * kPieces) {
+                    const int row = idx_s[t * kTile + r];
+                    src = (row >= 0 ? kv_b + (int64_t)row * kRowBytes : g_zero_row) + 16 * p;
+                }
+                gather16(src, (uint32_t)(uintptr_t)(base + blk * 1024));
+            }
+        }
+    };
+    // loads this wave issues per tile: blocks wave, wave + NWAVES, ... < 20
+    const int my_loads = (kTileBlocks - wave + NWAVES - 1) / NWAVES;
+
+    f32x4 acc_o[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;   // base of the exponentials for this lane's head (log2 units)
     float l_run = 0.f;         // partial sum of weights over this lane's tokens
 
-    // ---- gather staging: piece c = tid + k*NT of the tile -> (row r, piece p)
-    // With 4 waves the next tile is prefetched into registers while the current
-    // one is computed; with fewer waves the staging would not fit in registers,
-    // so the tile is loaded in batches right before it is used.
-    constexpr bool kPrefetch = NW == 4;
-    constexpr int KB = kPrefetch ? KPER : 5;           // pieces staged at once
-    u32x4 stage[KPER];
-    auto issue_loads = [&](int tile, int k0) {
-        const int t0 = t_begin + tile * kTile;
-#pragma unroll
-        for (int k = k0; k < (k0 + KB < KPER ? k0 + KB : KPER); k++) {
-            const int c = tid + k * NT;
-            const int r = c / kChunks, p = c - r * kChunks;
-            const int t = t0 + r;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (c < kTile * kChunks && t < t_end) {
-                const int row = idx_b[t];
-                if (row >= 0 && row < seqlen)
-                    v = *(const u32x4*)(kv_b + (int64_t)row * kRowBytes + 16 * p);
-            }
-            stage[k] = v;
-        }
-    };
-    auto store_stage = [&](int k0) {
-#pragma unroll
-        for (int k = k0; k < (k0 + KB < KPER ? k0 + KB : KPER); k++) {
-            const int c = tid + k * NT;
-            if (c >= kTile * kChunks) continue;
-            const int r = c / kChunks, p = c - r * kChunks;
-            const u32x4 v = stage[k];
-            if (p < 28) {
-                *(u32x4*)(lds.kr + r * kKrStride + 16 * p) = v;
-            } else if (p < 30) {
-                // group scales, slots 4(p-28)..4(p-28)+3; slot 7 (padding) is never
-                // read and becomes the rope factor.  A skipped row is all zeros and
-                // its weight is exactly 0, so its factors do not matter.
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int g = 4 * (p - 28) + j;
-                    const float s = g == 7 ? 1.f : __uint_as_float(v[j]);
-                    lds.sv[g][r] = s;
-                    lds.sq[g][r] = s * a.logit_factor;
-                }
-            } else {
-                *(u32x4*)(lds.kr + r * kKrStride + 16 * p) = v;
-                u32x4 h;
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    h[j] = pack_f16x2(bf16_bits_to_f32(v[j] & 0xffffu), bf16_bits_to_f32(v[j] >> 16));
-                *(u32x4*)(lds.ropeh + r * kRopeStride + 16 * (p - 30)) = h;
-            }
-        }
-    };
+    float* sT = sts[wave];
 
-    if (kPrefetch && ntiles > 0) issue_loads(0, 0);
+    int frontier = 0;
+    for (; frontier < NS - TW; frontier++) issue(frontier);
 
-    for (int tile = 0; tile < ntiles; tile++) {
-        // validity of the tile's 32 entries (lanes 0..31 of every wave)
-        const int t0 = t_begin + tile * kTile;
-        bool my_valid = false;
-        if (lane < kTile && t0 + lane < t_end) {
-            const int row = idx_b[t0 + lane];
-            my_valid = row >= 0 && row < seqlen;
-        }
+    for (int round = 0; round < nrounds; round++) {
+        for (; frontier < round * TW + NS; frontier++) issue(frontier);
+        // this wave's pieces of the round's tiles have landed (NS - TW tiles may
+        // still be in flight), then everyone else's
+        if (my_loads == G::PMAX) wait_vmcnt<(NS - TW) * G::PMAX>();
+        else wait_vmcnt<(NS - TW) * (G::PMAX - 1)>();
+        lds_barrier();
+
+        const int tile = round * TW + tw;
+        const uint8_t* st = ring + (tile % NS) * STAGE;
+        const bool my_valid = lane < kTile && idx_s[tile * kTile + lane] >= 0;
         const uint64_t vmask = __ballot(my_valid);
 
-        if (kPrefetch) {
-            store_stage(0);
-        } else {
-#pragma unroll
-            for (int k0 = 0; k0 < KPER; k0 += KB) {
-                issue_loads(tile, k0);
-                store_stage(k0);
-            }
-        }
-        __syncthreads();
-        if (kPrefetch && tile + 1 < ntiles) issue_loads(tile + 1, 0);
-
-        if (vmask != 0) {
-            // ---------------- S^T = K . Q^T for two 16-token halves
-            f32x4 s[2];
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++) {
-                const uint8_t* krow = lds.kr + (16 * tt + ln) * kKrStride;
-                f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int g = 0; g < 7; g++) {
-                    const u32x4 raw = *(const u32x4*)(krow + 64 * g + 16 * qg);
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[0], raw[1]), qn[g][0], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[2], raw[3]), qn[g][1], acc, 0, 0, 0);
-                    const f32x4 f = *(const f32x4*)&lds.sq[g][16 * tt + 4 * qg];
-                    sacc += f * acc;
-                }
-                {
-                    const u32x4 r0 = *(const u32x4*)(krow + 480 + 32 * qg);
-                    const u32x4 r1 = *(const u32x4*)(krow + 496 + 32 * qg);
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r0), qr[0], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r1), qr[1], acc, 0, 0, 0);
-                    const f32x4 f = *(const f32x4*)&lds.sq[7][16 * tt + 4 * qg];
-                    sacc += f * acc;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    if (!((vmask >> (16 * tt + 4 * qg + j)) & 1)) sacc[j] = -INFINITY;
-                s[tt] = sacc;
-            }
-
-            // ---------------- online softmax (log2 domain), lazy rescale
-            float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool need = mx > m_run + kTau;
-            if (__any(need)) {
-                const float m_new = need ? mx : m_run;
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < 32; i++) acc_o[i] *= alpha;
-            }
-            const float base = m_run == -INFINITY ? 0.f : m_run;
-            float p[2][4];
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    p[tt][j] = __builtin_amdgcn_exp2f(s[tt][j] - base);
-                    l_run += p[tt][j];
-                }
-
-            // ---------------- O^T += V^T . P^T, group by group
-            // tr8 source rows: lane 16q + j supplies token slot_token(8q + j/2), byte half j%2
-            const int tr_tok = slot_token(8 * qg + (ln >> 1));
-            const uint8_t* tr_row = lds.kr + tr_tok * kKrStride + 8 * (ln & 1);
-#pragma unroll
-            for (int g = 0; g < 8; g++) {
-                const f32x4 v0 = *(const f32x4*)&lds.sv[g][4 * qg];
-                const f32x4 v1 = *(const f32x4*)&lds.sv[g][16 + 4 * qg];
-                u32x4 bw;
-                bw[0] = pack_f16x2(p[0][0] * v0[0], p[0][1] * v0[1]);
-                bw[1] = pack_f16x2(p[0][2] * v0[2], p[0][3] * v0[3]);
-                bw[2] = pack_f16x2(p[1][0] * v1[0], p[1][1] * v1[1]);
-                bw[3] = pack_f16x2(p[1][2] * v1[2], p[1][3] * v1[3]);
-                f16x8 bop;
-                memcpy(&bop, &bw, 16);
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) {
-                    f16x8 aop;
-                    if (g < 7) {
-                        const lds_i32x2* src = (const lds_i32x2*)(tr_row + 64 * g + 16 * dt);
-                        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)src);
-                        aop = codes_to_f16((uint32_t)raw[0], (uint32_t)raw[1]);
-                    } else {
-                        // tr16: lane 16q + 4r + c supplies token slot_token(8q + r) (then 8q+4+r), columns 16dt + 4c..+3
-                        const int r = ln >> 2, cc = ln & 3;
-                        const uint8_t* base0 = lds.ropeh + slot_token(8 * qg + r) * kRopeStride + 2 * (16 * dt + 4 * cc);
-                        const uint8_t* base1 = lds.ropeh + slot_token(8 * qg + 4 + r) * kRopeStride + 2 * (16 * dt + 4 * cc);
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base0);
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base1);
-                        s16x4 both[2] = {lo, hi};
-                        memcpy(&aop, both, 16);
-                    }
-                    acc_o[4 * g + dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc_o[4 * g + dt], 0, 0, 0);
-                }
-            }
-        }
-        __syncthreads();
+        if (dh == 0)
+            compute_tile<0>(st, vmask, qop, acc_o, m_run, l_run, sT, xs[wave], xs[partner], lane,
+                            a.logit_factor);
+        else
+            compute_tile<1>(st, vmask, qop, acc_o, m_run, l_run, sT, xs[wave], xs[partner], lane,
+                            a.logit_factor);
+        lds_barrier();   // all waves are done with the round's slots before they are refilled
     }
+    wait_vmcnt<0>();     // trailing zero-row loads of the ring
 
-    // ---------------- epilogue: total weight, normalise, write
+    // ---------------- epilogue
     float l_tot = l_run;
     l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
+    if (TW > 1) {
+        // merge the token-parallel sets through LDS (the ring is free now)
+        __syncthreads();
+        float* mb = (float*)ring;   // [NHG*2][TW-1][64 lanes][16 tiles * 4 + 2]
+        constexpr int REC = 16 * 4 + 2;
+        const int pair_slot = hw * 2 + dh;
+        if (tw > 0) {
+            float* dst = mb + ((pair_slot * (TW - 1) + (tw - 1)) * 64 + lane) * REC;
+#pragma unroll
+            for (int i = 0; i < 16; i++) *(f32x4*)(dst + 4 * i) = acc_o[i];
+            dst[64] = m_run;
+            dst[65] = l_tot;
+        }
+        __syncthreads();
+        if (tw > 0) return;
+        float M = m_run;
+        for (int k = 0; k < TW - 1; k++)
+            M = fmaxf(M, mb[((pair_slot * (TW - 1) + k) * 64 + lane) * REC + 64]);
+        const float Ms = M == -INFINITY ? 0.f : M;
+        const float a0 = __builtin_amdgcn_exp2f(m_run - Ms);
+        l_tot *= a0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc_o[i] *= a0;
+        for (int k = 0; k < TW - 1; k++) {
+            const float* src = mb + ((pair_slot * (TW - 1) + k) * 64 + lane) * REC;
+            const float ak = __builtin_amdgcn_exp2f(src[64] - Ms);
+            l_tot += ak * src[65];
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc_o[i] += ak * *(const f32x4*)(src + 4 * i);
+        }
+        m_run = M;
+    }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
     const int64_t bh = (int64_t)b * a.heads + head;
     if (a.nsplit == 1 && !a.force_partials) {
-        uint16_t* o = a.out + bh * kLatent;
+        uint16_t* o = a.out + bh * kLatent + 256 * dh;
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
+        for (int i = 0; i < 16; i++) {
             const int d0 = 16 * i + 4 * qg;
             u32x2 w;
-            w[0] = pack_bf16x2_rne(acc_o[i][0] * inv, acc_o[i][1] * inv);
-            w[1] = pack_bf16x2_rne(acc_o[i][2] * inv, acc_o[i][3] * inv);
+            w[0] = pack_bf16x2(acc_o[i][0] * inv, acc_o[i][1] * inv);
+            w[1] = pack_bf16x2(acc_o[i][2] * inv, acc_o[i][3] * inv);
             *(u32x2*)(o + d0) = w;
         }
-        if (qg == 0) a.lse[bh] = lse2 * kLn2;
+        if (dh == 0 && qg == 0) a.lse[bh] = lse2 * kLn2;
     } else {
-        float* o = a.o_part + (bh * a.nsplit + split) * kLatent;
+        float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 256 * dh;
 #pragma unroll
-        for (int i = 0; i < 32; i++) *(f32x4*)(o + 16 * i + 4 * qg) = acc_o[i] * inv;
-        if (qg == 0) a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
+        for (int i = 0; i < 16; i++) *(f32x4*)(o + 16 * i + 4 * qg) = acc_o[i] * inv;
+        if (dh == 0 && qg == 0) a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
     }
 }
 
@@ -407,10 +533,10 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     u32x4 pk;
-    pk[0] = pack_bf16x2_rne(acc0[0] * inv, acc0[1] * inv);
-    pk[1] = pack_bf16x2_rne(acc0[2] * inv, acc0[3] * inv);
-    pk[2] = pack_bf16x2_rne(acc1[0] * inv, acc1[1] * inv);
-    pk[3] = pack_bf16x2_rne(acc1[2] * inv, acc1[3] * inv);
+    pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+    pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+    pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+    pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
     *(u32x4*)(out + (int64_t)row * kLatent + 8 * lane) = pk;
     if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
@@ -419,8 +545,9 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
 // host side
 
 struct Plan {
-    int nw;       // waves (16 heads each) per workgroup
-    int n_hg;     // head groups
+    int nhg;      // 16-head groups per workgroup
+    int tw;       // token-parallel wave sets per workgroup
+    int n_hg;     // head blocks (workgroups per sequence and split)
     int nsplit;
     int chunk;    // list entries per split (multiple of kTile)
 };
@@ -433,18 +560,22 @@ bool shape_ok(const smla_shape* s) {
 Plan make_plan(const smla_shape* s) {
     Plan p;
     const int k = s->num_heads / 16;
-    p.nw = k % 4 == 0 ? 4 : k % 3 == 0 ? 3 : k % 2 == 0 ? 2 : 1;
-    if (k == 0) p.nw = 1;
-    p.n_hg = k == 0 ? 0 : k / p.nw;
+    // head groups per workgroup: 4 when the heads allow it, else 3, 2, 1; the
+    // workgroup then has 8 waves (6 for 3 groups) through token-parallel sets
+    p.nhg = k % 4 == 0 ? 4 : k % 3 == 0 ? 3 : k % 2 == 0 ? 2 : 1;
+    if (k == 0) p.nhg = 1;
+    p.tw = p.nhg == 4 || p.nhg == 3 ? 1 : p.nhg == 2 ? 2 : 4;
+    p.n_hg = k == 0 ? 0 : k / p.nhg;
     const int tiles = (s->topk + kTile - 1) / kTile;
     int ns = s->num_splits;
     if (ns == 0) {
-        // fill the machine: about one workgroup per compute unit for 4-wave
-        // workgroups, four per compute unit for 1-wave workgroups
-        const int target = 256 * (p.nw == 4 ? 1 : p.nw == 1 ? 4 : 2);
+        // about one workgroup per compute unit
         const int base = s->batch * (p.n_hg > 0 ? p.n_hg : 1);
-        ns = base > 0 ? (target + base - 1) / base : 1;
+        ns = base > 0 ? (256 + base - 1) / base : 1;
     }
+    // the index chunk of a workgroup lives in LDS: at most kMaxChunk entries
+    const int min_ns = (s->topk + kMaxChunk - 1) / kMaxChunk;
+    if (ns < min_ns) ns = min_ns;
     if (ns > tiles) ns = tiles;
     if (ns < 1) ns = 1;
     const int per = (s->topk + ns - 1) / ns;
@@ -483,9 +614,9 @@ smla_status device_check() {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-template <int NW>
+template <int NHG, int TW>
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL(smla_decode_kernel<NW>, dim3(grid), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((smla_decode_kernel<NHG, TW>), dim3(grid), dim3(64 * NHG * 2 * TW), 0, st, a);
     return hipGetLastError();
 }
 
@@ -566,12 +697,14 @@ static smla_status prepare(const void* q, const void* kv_cache, const int32_t* t
 
 static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const int grid = a.batch * p.n_hg * p.nsplit;
+    DecodeArgs args = a;
+    args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     hipError_t e;
-    switch (p.nw) {
-        case 4: e = launch_decode<4>(a, grid, hs); break;
-        case 3: e = launch_decode<3>(a, grid, hs); break;
-        case 2: e = launch_decode<2>(a, grid, hs); break;
-        default: e = launch_decode<1>(a, grid, hs); break;
+    switch (p.nhg) {
+        case 4: e = launch_decode<4, 1>(args, grid, hs); break;
+        case 3: e = launch_decode<3, 1>(args, grid, hs); break;
+        case 2: e = launch_decode<2, 2>(args, grid, hs); break;
+        default: e = launch_decode<1, 4>(args, grid, hs); break;
     }
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
