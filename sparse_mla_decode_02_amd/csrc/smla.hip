@@ -6,16 +6,23 @@
 // "The Scale Indexing Complication"; "The 80KB Mystery", section "The Context:
 // Optimizing Attention on Blackwell"): each query token attends, with all heads
 // of this GPU, over the latent rows its top-k list selects; each row is read
-// from HBM once and shared by every head in one matrix product; the selected
-// list is split across workgroups (split-K) and the partial results merged
-// with a log-sum-exp combine.
+// from HBM once per group of 16 heads and shared by those heads in one matrix
+// product; the selected list is split across workgroups (split-K) when there
+// are too few (sequence, head group) pairs to fill the chip, and the partial
+// results are merged with a log-sum-exp combine.
 //
 // Design on gfx950 (differs from the Triton kernel of the pages, which pads
-// 448 to 512 because its tile ranges must be powers of two):
+// 448 to 512 because its tile ranges must be powers of two, and which stages
+// one tile per thread block through shared memory):
 //  * 448 = 7 groups x 64 columns = 14 MFMA K-steps of 32: no padding at all.
-//  * Workgroup = (sequence, group of up to 64 heads, split); one wave per 16
-//    heads.  A 32-token tile of raw cache rows is gathered into LDS once per
-//    workgroup with 16-byte loads and shared by all its waves.
+//  * Every wave is an independent decoder for 16 heads over the full 512-wide
+//    latent: it owns two 32-token LDS slots, gathers its next tile straight
+//    into one (global_load_lds, 16 bytes per lane, coalesced along the row)
+//    while it computes the current one from the other, and never waits for
+//    another wave until the end.  A workgroup is four such waves (one per
+//    SIMD, the whole 160 KB LDS) on the same (sequence, head group, split);
+//    they take the split's tiles round robin and merge their online-softmax
+//    states once, through LDS, at the end.
 //  * QK^T runs as S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the fp8 codes are
 //    converted exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with unit scale),
 //    q is used as stored, and each 64-column group's fp32 scale multiplies that
@@ -24,12 +31,14 @@
 //  * Online softmax in the log2 domain with lazy rescaling: the running base
 //    only moves when the tile maximum exceeds it by more than 8 (so weights
 //    stay below 2^8), which keeps the 128-register accumulator rescale rare.
+//    Cross-lane maxima use v_permlane16_swap / v_permlane32_swap (no LDS).
 //  * PV runs as O^T = V^T . P^T on v_mfma_f32_16x16x32_f16.  The S^T
 //    accumulator layout already is the P^T operand layout, so no data moves
 //    between lanes.  The group scale is folded into the weights
 //    (fp16(p * scale_g)), the value codes enter exactly (fp8 -> fp16), and the
 //    V^T operand is read from the row-major LDS tile with ds_read_b64_tr_b8
-//    (rope: ds_read_b64_tr_b16 from an fp16 copy made at gather time).
+//    (rope: ds_read_b64_tr_b16, bf16 values with the weight split into bf16
+//    high and low parts).
 //  * fp16 weights keep 11 significant bits, which bounds the value-product
 //    error by 2^-11 relative; bf16 weights (8 bits) would not meet 1e-2
 //    absolute on outputs near 4 once the bf16 output rounding is added.
@@ -57,19 +66,57 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kPieces = 39;                  // 16-byte pieces staged per row (608 payload + pad)
-constexpr int kRowLds = kPieces * 16;        // 624 bytes per token row in LDS
-constexpr int kTileBlocks = (kTile * kPieces + 63) / 64;   // 1 KB blocks per tile (20)
-constexpr int kMaxChunk = 2048;              // list entries per workgroup (index chunk in LDS)
+// LDS tile slot: 32 rows of codes and rope, row-major, kRowLds bytes apart,
+// followed by the tile's group scales transposed to [group][token].
+// LDS row: bytes 0..447 the fp8 codes, 448..575 the rope, 576..591 unused.
+// The pitch of 37 16-byte pieces makes the 16 rows read by one 16-lane group
+// start in 16 distinct 4-bank sets.  The scales arrive by a separate 4-byte
+// gather per (token, group), which writes the transposed table directly.
+constexpr int kPieces = 37;                         // LDS row pitch in 16-byte pieces
+constexpr int kCodePieces = 28;                     // pieces 0..27: codes; 28..35: rope
+constexpr int kRowLds = kPieces * 16;               // 592
+constexpr int kLdsRope = kNope;                     // rope offset inside an LDS row (448)
+constexpr int kScaleTable = kTile * kRowLds;        // scale table offset in a slot (18944)
+constexpr int kSlot = kScaleTable + 8 * kTile * 4;  // 19968 bytes per tile slot
+constexpr int kRowGathers = (kTile * kPieces + 63) / 64;   // 19 row gathers of 64 lanes
+constexpr int kScaleGathers = 4;                    // 4-byte gathers of the scale table
+constexpr int kWaves = 4;                           // waves per workgroup (one per SIMD)
+constexpr int kMaxChunk = 2048;                     // list entries of a shared-tile workgroup
+constexpr int kAccBytes = 32 * 64 * 16;             // one wave's output accumulator (32 KB)
 
-// A zero row: masked list entries are gathered from here, so every staged byte
-// is finite and a masked token contributes exactly zero.
-__device__ __attribute__((aligned(256))) uint8_t g_zero_row[kRowBytes];
+// Workgroup geometry for G head groups of 16 heads per workgroup (G = 1, 2, 4).
+// The four waves form T = 4 / G tile streams; stream s takes tiles s, s + T,
+// ... of the workgroup's chunk, and its G waves (one per head group) share
+// each of its tiles.  A stream owns a ring of NS tile slots.
+//  * G = 1: every wave is its own stream with two slots; it loads the rows of
+//    its next tile into registers one tile ahead and issues all gathers of a
+//    tile itself; no wave ever waits for another before the merge.
+//  * G = 2, 4: the chunk's (sanitised) list entries sit in an LDS table, every
+//    wave issues L of the tile's 23 gathers (one more, a no-op load, pads the
+//    count so that all waves count the same loads per tile), NS - 1 tiles are
+//    in flight, and a workgroup barrier per tile step recycles the slot of the
+//    previous step.
+template <int G>
+struct Geo {
+    static constexpr int T = kWaves / G;
+    static constexpr int NS = G == 1 ? 2 : G == 2 ? 3 : 7;
+    static constexpr int L = (kRowGathers + kScaleGathers + G - 1) / G;   // shared modes
+    static constexpr int kRing = T * NS * kSlot;
+    static constexpr int kIdx = kRing;                                   // index table
+    static constexpr int kDummy = kIdx + (G > 1 ? kMaxChunk * 4 : 0);    // no-op gather target
+    static constexpr int kEnd = kDummy + (G > 1 ? 1024 : 0);
+    static constexpr int kMerge = T > 1 ? kWaves * kAccBytes : 0;        // reuses the ring
+    static constexpr int kStat = kEnd > kMerge ? kEnd : kMerge;          // per-wave (max, sum)
+    static constexpr int kLds = kStat + kWaves * 32 * 4;
+    static_assert(kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static_assert(G == 1 || L * G <= kRowGathers + kScaleGathers + 1, "at most one no-op gather per tile");
+};
 
 __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -100,6 +147,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return u;
 }
 
+// Maximum / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48),
+// returned to every lane.  v_permlane16_swap with both operands equal leaves
+// rows (0,0,2,2) in one result and (1,1,3,3) in the other; v_permlane32_swap
+// leaves (0,1,0,1) and (2,3,2,3).  Both orders of each pair give the same sum.
+__device__ __forceinline__ float lanegroup_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(x);
+    const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+__device__ __forceinline__ float lanegroup_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(x);
+    const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Token held in MFMA k-slot `slot` (0..31) of a 32-token tile.  The S^T
 // accumulator of lane group q holds tokens 4q..4q+3 (first 16-token half) and
 // 16+4q..16+4q+3 (second half); the PV product uses k-slots 8q..8q+7 for them.
@@ -108,16 +177,51 @@ __device__ __forceinline__ int slot_token(int slot) {
     return r < 4 ? 4 * q + r : 16 + 4 * q + (r - 4);
 }
 
-// 16-byte gather of one lane straight into LDS at lds_base + 16 * lane
-// (global_load_lds_dwordx4; the LDS base goes through M0 and must be
-// wave-uniform).  Written as inline assembly so that the compiler does not
-// treat every later LDS read as dependent on every gather in flight; the
-// ordering is explicit instead: wait_vmcnt<N>() then lds_barrier().
-__device__ __forceinline__ void gather16(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// Buffer resource over one sequence's cache rows (gfx9 raw buffer, stride 0):
+// a gather addresses a row by a 32-bit byte offset, and the hardware range
+// check turns every offset at or past `bytes` into a load of zeros.  A masked
+// list entry therefore uses row -1: its offset is negative, i.e. above 2^32 -
+// 640 as an unsigned number, and it stages zeros (finite, contributes nothing).
+__device__ __forceinline__ i32x4 row_rsrc(const uint8_t* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(p >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Byte offset of 16-byte piece `off` of cache row `row` (row in [-1, 2^23)).
+__device__ __forceinline__ uint32_t row_offset(int row, int off) {
+    return (uint32_t)(__mul24(row, kRowBytes) + off);
+}
+
+// 16-byte (4-byte) gather of one lane straight into LDS at lds_base + 16 *
+// lane (+ 4 * lane): buffer_load_dwordx4 / _dword with the lds bit; the LDS
+// base goes through M0 and must be wave-uniform.  Written as inline assembly
+// so that the compiler does not treat every later LDS read as dependent on
+// every gather in flight; the ordering is explicit instead (s_waitcnt vmcnt
+// before a slot is read, and a workgroup barrier where slots are shared).
+__device__ __forceinline__ void gather16(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory", "m0");
+}
+
+__device__ __forceinline__ void gather4(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier without a memory fence: only this wave's LDS operations are
@@ -126,13 +230,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 struct DecodeArgs {
@@ -145,79 +242,135 @@ struct DecodeArgs {
     float* o_part;
     float* lse_part;
     int64_t kv_seq_stride;
+    uint32_t seq_bytes;   // kv_seq_stride * 640 (< 2^31): the range of a sequence's rows
     float logit_factor;   // scale * log2(e)
-    int32_t batch, heads, topk, nsplit, chunk, n_hg;
+    int32_t batch, heads, topk, nsplit, chunk, n_hb;
     int32_t force_partials;   // write split partials even when nsplit == 1
     int32_t xcd_remap;        // grid is a multiple of 8: keep a sequence's blocks on one XCD
 };
 
-// One 32-token tile for one wave: 16 heads x one latent half (DH = 0: nope
-// groups 0..3; DH = 1: nope groups 4..6 and the rope).  st is the tile's ring
-// slot (32 raw rows, kRowLds apart); vmask marks the kept tokens.  The partial
-// logits of the two halves are exchanged through xs_mine / xs_other, and the
-// caller's workgroup barrier separates the write from the partner's read.
-template <int DH>
-__device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, const bf16x8 (&qop)[8],
-                                             f32x4 (&acc_o)[16], float& m_run, float& l_run,
-                                             float* sT, float* xs_mine, const float* xs_other,
-                                             int lane, float logit_factor) {
-    constexpr int G0 = 4 * DH;           // first nope group
-    constexpr int NG = DH == 0 ? 4 : 3;  // nope groups
+// Source byte offset inside a cache row of LDS piece p: pieces 0..27 are the
+// codes, 28..35 the rope (cache pieces 30..37), 36 the unused pitch padding
+// (cache piece 38).
+__device__ __forceinline__ int piece_src(int p) { return 16 * (p < kCodePieces ? p : p + 2); }
+
+// G = 1: gather one whole 32-token tile into the LDS slot at slot_lds.  Every
+// lane holds the (sanitised) row of token (lane & 31).  Row gather k covers
+// the slot's bytes [1024k, 1024k + 1024): lane l loads LDS piece p = c % 37 of
+// token r = c / 37 (c = 64k + l), whose row comes from lane r by ds_bpermute.
+// Scale gather k' loads scale 2k' + (l >> 5) of token l & 31 into the table.
+__device__ __forceinline__ void issue_tile_own(int row_of_lane, i32x4 rsrc, uint32_t slot_lds, int lane_in) {
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));   // keep the per-lane piece walk inside the loop (registers)
+    int r = 0;
+    int p = lane;
+    if (p >= kPieces) {
+        p -= kPieces;
+        r = 1;
+    }
+    int rows[kRowGathers];
+    int offs[kRowGathers];
+#pragma unroll
+    for (int k = 0; k < kRowGathers; k++) {
+        rows[k] = __builtin_amdgcn_ds_bpermute(4 * (r & 31), row_of_lane);
+        offs[k] = piece_src(p);
+        // next piece: c + 64 = c + 37 + 27
+        p += 27;
+        r += 1;
+        if (p >= kPieces) {
+            p -= kPieces;
+            r += 1;
+        }
+    }
+    // all lookups are issued before the first one is used
+#pragma unroll
+    for (int k = 0; k < kRowGathers; k++) asm volatile("" : "+v"(rows[k]));
+#pragma unroll
+    for (int k = 0; k < kScaleGathers; k++)
+        gather4(row_offset(row_of_lane, SMLA_SCALE_OFFSET + 4 * (2 * k + (lane >> 5))), rsrc,
+                slot_lds + kScaleTable + 256 * k);
+#pragma unroll
+    for (int k = 0; k < kRowGathers; k++)
+        if (k + 1 < kRowGathers || lane < kTile * kPieces - 64 * (kRowGathers - 1))
+            gather16(row_offset(rows[k], offs[k]), rsrc, slot_lds + 1024 * k);
+}
+
+// G = 2, 4: this wave's gathers of a tile are ids hgl, hgl + G, ... (L of
+// them): 0..18 row gathers, 19..22 scale gathers, anything else a no-op load
+// of zeros into the dummy area.  rows points at the tile's 32 entries of the
+// LDS index table; live = false gathers zeros.  The table lookups are all
+// issued before the first gather.
+template <int G, int L>
+__device__ __forceinline__ void issue_tile_shared(const int32_t* rows, bool live, i32x4 rsrc, uint32_t slot_lds,
+                                                  uint32_t dummy_lds, int hgl, int lane) {
+    int row[L];
+#pragma unroll
+    for (int u = 0; u < L; u++) {
+        const int id = hgl + G * u;
+        const int c = 64 * id + lane;
+        const int r = id < kRowGathers ? (c * 1772) >> 16 : lane;   // c / 37 for c < 1216
+        row[u] = rows[r & 31];
+    }
+#pragma unroll
+    for (int u = 0; u < L; u++) asm volatile("" : "+v"(row[u]));
+#pragma unroll
+    for (int u = 0; u < L; u++) {
+        const int id = hgl + G * u;
+        const int rw = live ? row[u] : -1;
+        if (id < kRowGathers) {
+            const int c = 64 * id + lane;
+            const int p = c - kPieces * ((c * 1772) >> 16);
+            if (c < kTile * kPieces) gather16(row_offset(rw, piece_src(p)), rsrc, slot_lds + 1024 * id);
+        } else if (id < kRowGathers + kScaleGathers) {
+            const int k = id - kRowGathers;
+            gather4(row_offset(rw, SMLA_SCALE_OFFSET + 4 * (2 * k + (lane >> 5))), rsrc,
+                    slot_lds + kScaleTable + 256 * k);
+        } else {
+            gather4(0x80000000u, rsrc, dummy_lds);
+        }
+    }
+}
+
+// One 32-token tile for one wave: 16 heads x the full latent.  st is the
+// tile's LDS slot; vmask marks the kept tokens.
+__device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, const bf16x8 (&qop)[16],
+                                             f32x4 (&acc_o)[32], float& m_run, float& l_run, int lane,
+                                             float logit_factor) {
     const int qg = lane >> 4, ln = lane & 15;
 
-    // group scales of this half, transposed to [group][token] in this wave's
-    // own LDS block (a wave's LDS operations complete in order)
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        const int e = lane + 64 * k;          // 0..127: token e / 4, group G0 + e % 4
-        const int t = e >> 2, g = e & 3;
-        if (g < NG) sT[g * kTile + t] = *(const float*)(st + t * kRowLds + SMLA_SCALE_OFFSET + 4 * (G0 + g));
-    }
+    // group scales, transposed: sT[g * 32 + t] = scale g of token t
+    const float* sT = (const float*)(st + kScaleTable);
 
-    // ---------------- partial S^T over this half's columns, per 16-token half:
-    // operands read first, then one MFMA chain per group (independent chains)
+    // ---------------- S^T = K . Q^T per 16-token half; lane group q takes
+    // columns 16q..16q+15 of every 64-column group (two K-steps of 8), and rope
+    // columns 16q..16q+15
     f32x4 s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
         const uint8_t* krow = st + (16 * tt + ln) * kRowLds;
-        u32x4 raw[NG];
-        u32x4 rrope[2];
+        u32x4 raw[7];
+        u32x4 rr[2];
 #pragma unroll
-        for (int g = 0; g < NG; g++) raw[g] = *(const u32x4*)(krow + 64 * (G0 + g) + 16 * qg);
-        if (DH == 1) {
-            rrope[0] = *(const u32x4*)(krow + SMLA_ROPE_OFFSET + 32 * qg);
-            rrope[1] = *(const u32x4*)(krow + SMLA_ROPE_OFFSET + 16 + 32 * qg);
-        }
-        f32x4 acc[NG + 1];
+        for (int g = 0; g < 7; g++) raw[g] = *(const u32x4*)(krow + 64 * g + 16 * qg);
+        rr[0] = *(const u32x4*)(krow + kLdsRope + 32 * qg);
+        rr[1] = *(const u32x4*)(krow + kLdsRope + 32 * qg + 16);
+        f32x4 acc[8];
 #pragma unroll
-        for (int g = 0; g < NG; g++)
+        for (int g = 0; g < 7; g++)
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][0], raw[g][1]), qop[2 * g],
                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        if (DH == 1)
-            acc[NG] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rrope[0]), qop[6],
-                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[0]), qop[14], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                         0, 0, 0);
 #pragma unroll
-        for (int g = 0; g < NG; g++)
+        for (int g = 0; g < 7; g++)
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][2], raw[g][3]), qop[2 * g + 1],
                                                              acc[g], 0, 0, 0);
-        if (DH == 1)
-            acc[NG] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rrope[1]), qop[7], acc[NG], 0, 0, 0);
-        f32x4 v = DH == 1 ? acc[NG] : f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[1]), qop[15], acc[7], 0, 0, 0);
+        f32x4 v = acc[7];
 #pragma unroll
-        for (int g = 0; g < NG; g++) v += *(const f32x4*)(sT + g * kTile + 16 * tt + 4 * qg) * acc[g];
+        for (int g = 0; g < 7; g++)
+            v += *(const f32x4*)(sT + g * kTile + 16 * tt + 4 * qg) * acc[g];
         s[tt] = v;
-    }
-
-    // exchange with the partner wave; both form S = S_half0 + S_half1 in the
-    // same order, so both hold bit-identical logits
-    *(f32x4*)(xs_mine + 8 * lane) = s[0];
-    *(f32x4*)(xs_mine + 8 * lane + 4) = s[1];
-    lds_barrier();
-    {
-        const f32x4 o0 = *(const f32x4*)(xs_other + 8 * lane);
-        const f32x4 o1 = *(const f32x4*)(xs_other + 8 * lane + 4);
-        s[0] = DH == 0 ? s[0] + o0 : o0 + s[0];
-        s[1] = DH == 0 ? s[1] + o1 : o1 + s[1];
     }
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
@@ -230,16 +383,18 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
     // ---------------- online softmax (log2 domain), lazy rescale
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = lanegroup_max(mx);
     const bool need = mx > m_run + kTau;
     if (__any(need)) {
         const float m_new = need ? mx : m_run;
         const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        m_run = m_new;
-        l_run *= alpha;
+        // the first kept tokens only set the base: the accumulators are still zero
+        if (__any(m_run != -INFINITY)) {
+            l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; i++) acc_o[i] *= alpha;
+            for (int i = 0; i < 32; i++) acc_o[i] *= alpha;
+        }
+        m_run = m_new;
     }
     const float base = m_run == -INFINITY ? 0.f : m_run;
     float p[8];   // k-slot order: tokens 4q+j (j < 4), then 16+4q+(j-4)
@@ -249,30 +404,18 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
         l_run += p[j];
     }
 
-    // ---------------- O^T += V^T . P^T over this half's columns
+    // ---------------- O^T += V^T . P^T
     // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2), byte half j%2
     const uint8_t* tr_row = st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1);
-    s16x4 rv[4][2];
-    if (DH == 1) {
-        // rope V^T via tr16: lane 16q + 4r + c supplies slot_token(8q + r), then (8q + 4 + r)
-        const int col = 8 * (ln & 3);
-        const uint8_t* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + SMLA_ROPE_OFFSET + col;
-        const uint8_t* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + SMLA_ROPE_OFFSET + col;
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-            rv[dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
-            rv[dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
-        }
-    }
-#pragma unroll
-    for (int g = 0; g < NG; g++) {
+    for (int g = 0; g < 7; g++) {
         i32x2 vraw[4];
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++)
-            vraw[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * (G0 + g) + 16 * dt));
+        for (int cb = 0; cb < 4; cb++)
+            vraw[cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * g + 16 * cb));
+        // weights fp16(p * scale_g); exact fp8 -> fp16 value codes
         const f32x4 sv0 = *(const f32x4*)(sT + g * kTile + 4 * qg);
         const f32x4 sv1 = *(const f32x4*)(sT + g * kTile + 16 + 4 * qg);
-        // weights fp16(p * scale_g); exact fp8 -> fp16 value codes
         f16x8 bop;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -280,12 +423,23 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
             bop[4 + j] = (_Float16)(p[4 + j] * sv1[j]);
         }
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++)
-            acc_o[4 * g + dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                codes_to_f16((uint32_t)vraw[dt][0], (uint32_t)vraw[dt][1]), bop, acc_o[4 * g + dt], 0, 0, 0);
+        for (int cb = 0; cb < 4; cb++)
+            acc_o[4 * g + cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                codes_to_f16((uint32_t)vraw[cb][0], (uint32_t)vraw[cb][1]), bop, acc_o[4 * g + cb], 0, 0, 0);
     }
-    if (DH == 1) {
-        // rope: bf16 values as stored; weights split into bf16 high and low parts
+    {
+        // rope V^T via tr16: lane 16q + 4r + c supplies slot_token(8q + r), then
+        // slot_token(8q + 4 + r), columns 4c..4c+3 of each 16-column block
+        const int col = 8 * (ln & 3);
+        const uint8_t* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col;
+        const uint8_t* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col;
+        s16x4 rv[4][2];
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            rv[dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
+            rv[dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
+        }
+        // bf16 values as stored; weights split into bf16 high and low parts
         bf16x8 phi, plo;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -297,214 +451,218 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
         for (int dt = 0; dt < 4; dt++) {
             bf16x8 aop;
             memcpy(&aop, rv[dt], 16);
-            f32x4 c = acc_o[12 + dt];
+            f32x4 c = acc_o[28 + dt];
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, c, 0, 0, 0);
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, c, 0, 0, 0);
-            acc_o[12 + dt] = c;
+            acc_o[28 + dt] = c;
         }
     }
 }
 
-// Workgroup geometry.  A workgroup covers NHG groups of 16 heads.  Each head
-// group is served by a pair of waves, one per latent half: half 0 holds nope
-// groups 0..3 (columns 0..255), half 1 holds nope groups 4..6 and the rope
-// (columns 256..511).  TW such sets of pairs take different tiles of the list
-// (token-parallel) and are merged at the end.  Each wave thus holds half of
-// its heads' query (32 registers) and half of their output accumulator (64
-// registers), which lets two waves share a SIMD.
-template <int NHG, int TW>
-struct Geo {
-    static constexpr int NWAVES = NHG * 2 * TW;
-    static constexpr int NT = 64 * NWAVES;
-    static constexpr int STAGE = kTileBlocks * 1024;              // one tile of raw rows
-    static constexpr int NS = TW == 1 ? 5 : 6;                    // ring stages
-    static constexpr int PMAX = (kTileBlocks + NWAVES - 1) / NWAVES;   // loads per wave per tile
-    static constexpr int XS = NWAVES * 64 * 8 * 4;                // partial-logit exchange
-    static constexpr int ST = NWAVES * 4 * kTile * 4;             // per-wave transposed scales
-};
+// The query and the output accumulator stay in AGPRs across tiles (the MFMAs
+// read and write them there); VGPRs hold the per-tile work.
+__device__ __forceinline__ void pin_state(bf16x8 (&qop)[16], f32x4 (&acc_o)[32]) {
+#pragma unroll
+    for (int k = 0; k < 16; k++) asm volatile("" : "+a"(qop[k]));
+#pragma unroll
+    for (int k = 0; k < 32; k++) asm volatile("" : "+a"(acc_o[k]));
+}
 
-// One workgroup = (sequence b, head block hb, split s).  Rows of the split's
-// list are gathered straight into an LDS ring of NS tiles (global_load_lds,
-// 16 bytes per lane), NS - TW tiles in flight while TW tiles are computed.
-template <int NHG, int TW>
-__global__ __launch_bounds__(64 * NHG * 2 * TW, 2) void smla_decode_kernel(DecodeArgs a) {
-    using G = Geo<NHG, TW>;
-    constexpr int NWAVES = G::NWAVES, NT = G::NT, STAGE = G::STAGE, NS = G::NS;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
-    __shared__ int32_t idx_s[kMaxChunk + TW * kTile];   // padded to whole rounds
-    __shared__ __attribute__((aligned(16))) float xs[NWAVES][64 * 8];
-    __shared__ __attribute__((aligned(16))) float sts[NWAVES][4 * kTile];
+// One workgroup = (sequence b, head block hb of G x 16 heads, split); see Geo
+// for how its four waves share the split's tiles.  At the end the T streams'
+// states of each head group are merged through LDS and the workgroup writes
+// the split's normalised output and log-sum-exp (or the final bf16 result).
+template <int G>
+__global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs a) {
+    using Ge = Geo<G>;
+    constexpr int T = Ge::T, NS = Ge::NS;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Ge::kLds];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int dh = wave & 1;                   // latent half
-    const int hw = (wave >> 1) % NHG;          // head group within the block
-    const int tw = (wave >> 1) / NHG;          // token-parallel set
-    const int partner = wave ^ 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qg = lane >> 4;                  // lane group 0..3
     const int ln = lane & 15;                  // head column of the 16x16 tiles
-    const int g0 = 4 * dh;                     // first nope group of this half
-    const int ng = dh == 0 ? 4 : 3;            // nope groups of this half
+    const int strm = wave / G;                 // tile stream
+    const int hgl = wave % G;                  // head group within the workgroup
 
     int bid = blockIdx.x;
     if (a.xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-    const int hb = bid % a.n_hg;
-    bid /= a.n_hg;
     const int split = bid % a.nsplit;
-    const int b = bid / a.nsplit;
+    bid /= a.nsplit;
+    const int hb = bid % a.n_hb;
+    const int b = bid / a.n_hb;
 
-    const int head = hb * (16 * NHG) + 16 * hw + ln;
+    const int head = 16 * (G * hb + hgl) + ln;
     const int t_begin = split * a.chunk;
-    const int t_end = min(a.topk, t_begin + a.chunk);
-    const int n_ent = max(t_end - t_begin, 0);
+    const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
     const int ntiles = (n_ent + kTile - 1) / kTile;
-    const int nrounds = (ntiles + TW - 1) / TW;
     const int seqlen = a.seqlens[b];
-    const uint8_t* kv_b = a.kv + (int64_t)b * a.kv_seq_stride * kRowBytes;
+    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * kRowBytes, a.seq_bytes);
+    const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
 
-    // ---- index chunk -> LDS: the cache row of each entry, or -1 when masked
-    {
-        const int32_t* src = a.idx + (int64_t)b * a.topk + t_begin;
-        for (int i = tid; i < nrounds * TW * kTile; i += NT) {
+    // ---- the query of this lane's head as the B operand of S^T = K . Q^T
+    // (k-slot order matches the K reads: lane group q takes columns 16q..16q+15
+    // of every 64-column group, 8 per K-step, and rope columns 16q..16q+15).
+    // Loaded after the first tile's gathers are issued; pin_state then makes
+    // the compiler wait for it once, before the tile loop.
+    bf16x8 qop[16];
+    auto load_query = [&]() {
+        const uint16_t* qh = a.q + ((int64_t)b * a.heads + head) * kLatent;
+#pragma unroll
+        for (int g = 0; g < 7; g++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+                qop[2 * g + ks] = as_bf16x8(*(const u32x4*)(qh + 64 * g + 16 * qg + 8 * ks));
+        qop[14] = as_bf16x8(*(const u32x4*)(qh + kNope + 16 * qg));
+        qop[15] = as_bf16x8(*(const u32x4*)(qh + kNope + 16 * qg + 8));
+    };
+
+    f32x4 acc_o[32];
+#pragma unroll
+    for (int i = 0; i < 32; i++) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;   // base of the exponentials for this lane's head (log2 units)
+    float l_run = 0.f;         // partial sum of weights over this lane's tokens
+
+    if constexpr (G == 1) {
+        // ---- independent waves: tiles wave, wave + 4, ...; rows one tile ahead
+        const int my_n = wave < ntiles ? (ntiles - 1 - wave) / kWaves + 1 : 0;
+        uint8_t* my_lds = lds + wave * NS * kSlot;
+        const uint32_t my_lds_addr = (uint32_t)(uintptr_t)my_lds;
+        auto tile_row = [&](int i) -> int {   // sanitised row of token (lane & 31) of tile i
+            const int e = (wave + kWaves * i) * kTile + (lane & 31);
+            int row = -1;
+            if (e < n_ent) {
+                row = idx_b[e];
+                if (row < 0 || row >= seqlen) row = -1;
+            }
+            return row;
+        };
+        int row_cur = -1, row_next = -1;
+        if (my_n > 0) {
+            row_cur = tile_row(0);
+            issue_tile_own(row_cur, rsrc, my_lds_addr, lane);
+        }
+        load_query();
+        pin_state(qop, acc_o);
+        if (my_n > 1) row_next = tile_row(1);
+        for (int i = 0; i < my_n; i++) {
+            pin_state(qop, acc_o);
+            wait_vmcnt<0>();   // tile i is in its slot; the rows of tile i + 1 are in registers
+            if (i + 1 < my_n) issue_tile_own(row_next, rsrc, my_lds_addr + ((i + 1) & 1) * kSlot, lane);
+            const int row_after = i + 2 < my_n ? tile_row(i + 2) : -1;
+            const uint64_t vmask = __ballot(lane < kTile && row_cur >= 0);
+            compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor);
+            row_cur = row_next;
+            row_next = row_after;
+        }
+        wait_vmcnt<0>();
+    } else {
+        // ---- shared tiles: sanitised index table, NS-slot ring per stream
+        int32_t* idx_s = (int32_t*)(lds + Ge::kIdx);
+        for (int i = threadIdx.x; i < ntiles * kTile; i += 64 * kWaves) {
             int row = -1;
             if (i < n_ent) {
-                row = src[i];
+                row = idx_b[i];
                 if (row < 0 || row >= seqlen) row = -1;
             }
             idx_s[i] = row;
         }
-    }
-    // ---- this half of the query as the B operand of S^T = K . Q^T
-    // (k-slot order matches the K reads: lane group q takes columns 16q..16q+15
-    // of every 64-column group, 8 per K-step)
-    bf16x8 qop[8];
-    {
-        const uint16_t* qh = a.q + ((int64_t)b * a.heads + head) * kLatent + 256 * dh;
+        __syncthreads();
+        const int nsteps = (ntiles + T - 1) / T;
+        uint8_t* ring = lds + strm * NS * kSlot;
+        const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+        const uint32_t dummy_addr = (uint32_t)(uintptr_t)(lds + Ge::kDummy);
+        auto issue_step = [&](int step) {
+            const int tile = strm + T * step;
+            const bool live = tile < ntiles;
+            const int32_t* rows = idx_s + (live ? tile : 0) * kTile;
+            const uint32_t slot = ring_addr + (step % NS) * kSlot;
+            issue_tile_shared<G, Ge::L>(rows, live, rsrc, slot, dummy_addr, hgl, lane);
+        };
+        issue_step(0);
+        load_query();
+        pin_state(qop, acc_o);
 #pragma unroll
-        for (int g = 0; g < 4; g++)
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++)
-                qop[2 * g + ks] = as_bf16x8(*(const u32x4*)(qh + 64 * g + 16 * qg + 8 * ks));
+        for (int st = 1; st < NS - 1; st++) issue_step(st);
+        // at least one step even for an empty split (it computes a zero-filled
+        // slot with no kept token), so the accumulators have a single path
+        int step = 0;
+        do {
+            pin_state(qop, acc_o);
+            wait_vmcnt<(NS - 2) * Ge::L>();   // this wave's gathers of this step's tile have landed
+            lds_barrier();                    // ... and everyone's; the previous step's slot is free
+            issue_step(step + NS - 1);
+            // a stream past the end of the chunk (G = 2, last step) computes its
+            // zero-filled slot with no kept token, which changes nothing
+            const int tile = strm + T * step;
+            const bool live = tile < ntiles;
+            const uint64_t vmask = __ballot(live && lane < kTile && idx_s[(live ? tile : 0) * kTile + (lane & 31)] >= 0);
+            compute_tile(ring + (step % NS) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor);
+        } while (++step < nsteps);
+        wait_vmcnt<0>();   // trailing no-op loads of the ring
     }
-    wait_vmcnt<0>();
-    __syncthreads();
 
-    // ---- gather of tile t into ring slot t % NS.  The tile is 1248 16-byte
-    // pieces (32 rows x 39); piece c is row c/39, piece c%39, placed at byte 16c
-    // of the slot.  1 KB block k of the slot is loaded by wave k % NWAVES.
-    // Pieces past the tile and tiles past the end load the zero row, so each
-    // wave issues the same number of loads for every tile.
-    auto issue = [&](int t) {
-        uint8_t* base = ring + (t % NS) * STAGE;
+    // ---------------- merge of the T streams of each head group
+    const float l_tot = lanegroup_sum(l_run);
+    float M = m_run, L = l_tot;
+    if constexpr (T > 1) {
+        __syncthreads();   // every wave is done with the ring (the merge reuses it)
+        float* stat = (float*)(lds + Ge::kStat);   // [wave][max 16 | sum 16]
+        if (lane < 16) {
+            stat[wave * 32 + lane] = m_run;
+            stat[wave * 32 + 16 + lane] = l_tot;
+        }
+        __syncthreads();
+        M = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < G::PMAX; k++) {
-            const int blk = k * NWAVES + wave;
-            if (blk < kTileBlocks) {
-                const int c = blk * 64 + lane;
-                const int r = c / kPieces;
-                const int p = c - r * kPieces;
-                const uint8_t* src = g_zero_row;
-                if (t < ntiles && c < kTile * kPieces) {
-                    const int row = idx_s[t * kTile + r];
-                    src = (row >= 0 ? kv_b + (int64_t)row * kRowBytes : g_zero_row) + 16 * p;
-                }
-                gather16(src, (uint32_t)(uintptr_t)(base + blk * 1024));
-            }
+        for (int s2 = 0; s2 < T; s2++) M = fmaxf(M, stat[(s2 * G + hgl) * 32 + ln]);
+        const float Ms0 = M == -INFINITY ? 0.f : M;
+        L = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < T; s2++)
+            L += __builtin_amdgcn_exp2f(stat[(s2 * G + hgl) * 32 + ln] - Ms0) * stat[(s2 * G + hgl) * 32 + 16 + ln];
+        const float aw = __builtin_amdgcn_exp2f(m_run - Ms0);
+        f32x4* part = (f32x4*)(lds + wave * kAccBytes);
+#pragma unroll
+        for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i] * aw;
+        __syncthreads();
+    }
+
+    // stream s finishes accumulator blocks [s * 32 / T, (s + 1) * 32 / T) of its
+    // head group; block i holds columns 16i + 4qg + j for head ln
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float lse2 = L > 0.f ? M + log2f(L) : -INFINITY;
+    const int64_t bh = (int64_t)b * a.heads + head;
+    const bool final_out = a.nsplit == 1 && !a.force_partials;
+    auto block_sum = [&](int i) -> f32x4 {
+        if constexpr (T > 1) {
+            f32x4 v = ((const f32x4*)(lds + hgl * kAccBytes))[i * 64 + lane];
+#pragma unroll
+            for (int s2 = 1; s2 < T; s2++) v += ((const f32x4*)(lds + (s2 * G + hgl) * kAccBytes))[i * 64 + lane];
+            return v;
+        } else {
+            return acc_o[i];
         }
     };
-    // loads this wave issues per tile: blocks wave, wave + NWAVES, ... < 20
-    const int my_loads = (kTileBlocks - wave + NWAVES - 1) / NWAVES;
-
-    f32x4 acc_o[16];
+    const int i0 = T == 1 ? 0 : strm * (32 / T);   // static index when T == 1
+    if (final_out) {
+        uint16_t* o = a.out + bh * kLatent + 4 * qg;
 #pragma unroll
-    for (int i = 0; i < 16; i++) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;   // base of the exponentials for this lane's head (log2 units)
-    float l_run = 0.f;         // partial sum of weights over this lane's tokens
-
-    float* sT = sts[wave];
-
-    int frontier = 0;
-    for (; frontier < NS - TW; frontier++) issue(frontier);
-
-    for (int round = 0; round < nrounds; round++) {
-        for (; frontier < round * TW + NS; frontier++) issue(frontier);
-        // this wave's pieces of the round's tiles have landed (NS - TW tiles may
-        // still be in flight), then everyone else's
-        if (my_loads == G::PMAX) wait_vmcnt<(NS - TW) * G::PMAX>();
-        else wait_vmcnt<(NS - TW) * (G::PMAX - 1)>();
-        lds_barrier();
-
-        const int tile = round * TW + tw;
-        const uint8_t* st = ring + (tile % NS) * STAGE;
-        const bool my_valid = lane < kTile && idx_s[tile * kTile + lane] >= 0;
-        const uint64_t vmask = __ballot(my_valid);
-
-        if (dh == 0)
-            compute_tile<0>(st, vmask, qop, acc_o, m_run, l_run, sT, xs[wave], xs[partner], lane,
-                            a.logit_factor);
-        else
-            compute_tile<1>(st, vmask, qop, acc_o, m_run, l_run, sT, xs[wave], xs[partner], lane,
-                            a.logit_factor);
-        lds_barrier();   // all waves are done with the round's slots before they are refilled
-    }
-    wait_vmcnt<0>();     // trailing zero-row loads of the ring
-
-    // ---------------- epilogue
-    float l_tot = l_run;
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (TW > 1) {
-        // merge the token-parallel sets through LDS (the ring is free now)
-        __syncthreads();
-        float* mb = (float*)ring;   // [NHG*2][TW-1][64 lanes][16 tiles * 4 + 2]
-        constexpr int REC = 16 * 4 + 2;
-        const int pair_slot = hw * 2 + dh;
-        if (tw > 0) {
-            float* dst = mb + ((pair_slot * (TW - 1) + (tw - 1)) * 64 + lane) * REC;
-#pragma unroll
-            for (int i = 0; i < 16; i++) *(f32x4*)(dst + 4 * i) = acc_o[i];
-            dst[64] = m_run;
-            dst[65] = l_tot;
-        }
-        __syncthreads();
-        if (tw > 0) return;
-        float M = m_run;
-        for (int k = 0; k < TW - 1; k++)
-            M = fmaxf(M, mb[((pair_slot * (TW - 1) + k) * 64 + lane) * REC + 64]);
-        const float Ms = M == -INFINITY ? 0.f : M;
-        const float a0 = __builtin_amdgcn_exp2f(m_run - Ms);
-        l_tot *= a0;
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc_o[i] *= a0;
-        for (int k = 0; k < TW - 1; k++) {
-            const float* src = mb + ((pair_slot * (TW - 1) + k) * 64 + lane) * REC;
-            const float ak = __builtin_amdgcn_exp2f(src[64] - Ms);
-            l_tot += ak * src[65];
-#pragma unroll
-            for (int i = 0; i < 16; i++) acc_o[i] += ak * *(const f32x4*)(src + 4 * i);
-        }
-        m_run = M;
-    }
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-    const int64_t bh = (int64_t)b * a.heads + head;
-    if (a.nsplit == 1 && !a.force_partials) {
-        uint16_t* o = a.out + bh * kLatent + 256 * dh;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int d0 = 16 * i + 4 * qg;
+        for (int ii = 0; ii < 32 / T; ii++) {
+            const f32x4 v = block_sum(i0 + ii);
             u32x2 w;
-            w[0] = pack_bf16x2(acc_o[i][0] * inv, acc_o[i][1] * inv);
-            w[1] = pack_bf16x2(acc_o[i][2] * inv, acc_o[i][3] * inv);
-            *(u32x2*)(o + d0) = w;
+            w[0] = pack_bf16x2(v[0] * inv, v[1] * inv);
+            w[1] = pack_bf16x2(v[2] * inv, v[3] * inv);
+            *(u32x2*)(o + 16 * (i0 + ii)) = w;
         }
-        if (dh == 0 && qg == 0) a.lse[bh] = lse2 * kLn2;
     } else {
-        float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 256 * dh;
+        float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 4 * qg;
 #pragma unroll
-        for (int i = 0; i < 16; i++) *(f32x4*)(o + 16 * i + 4 * qg) = acc_o[i] * inv;
-        if (dh == 0 && qg == 0) a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
+        for (int ii = 0; ii < 32 / T; ii++) *(f32x4*)(o + 16 * (i0 + ii)) = block_sum(i0 + ii) * inv;
+    }
+    if (strm == 0 && qg == 0) {
+        if (final_out) a.lse[bh] = lse2 * kLn2;
+        else a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
     }
 }
 
@@ -545,36 +703,55 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
 // host side
 
 struct Plan {
-    int nhg;      // 16-head groups per workgroup
-    int tw;       // token-parallel wave sets per workgroup
-    int n_hg;     // head blocks (workgroups per sequence and split)
+    int g;        // 16-head groups per workgroup (1, 2 or 4)
+    int n_hb;     // head blocks (workgroups per sequence and split)
     int nsplit;
     int chunk;    // list entries per split (multiple of kTile)
 };
 
+// Rows of one sequence are addressed by 32-bit byte offsets below 2^31.
+constexpr int64_t kMaxSeqStride = ((int64_t)1 << 31) / kRowBytes;
+
 bool shape_ok(const smla_shape* s) {
     return s && s->batch >= 0 && s->num_heads >= 0 && s->num_heads % 16 == 0 &&
-           s->num_heads <= 256 && s->topk >= 0 && s->num_splits >= 0 && s->kv_seq_stride >= 1;
+           s->num_heads <= 256 && s->topk >= 0 && s->num_splits >= 0 && s->kv_seq_stride >= 1 &&
+           s->kv_seq_stride <= kMaxSeqStride;
+}
+
+constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
+
+// Split count when the caller leaves it to the library.  A workgroup's time is
+// taken as (tile steps + 1) tile times, where a step is T tiles of the split
+// (T = 4 / g), a launch as that times the number of rounds of kComputeUnits
+// workgroups, and any split adds one tile time for the partials and the
+// combine.  Ties go to fewer splits.  min_ns bounds the split size from below.
+int choose_splits(int base, int tiles, int t_streams, int min_ns) {
+    if (base <= 0 || tiles <= 1) return 1;
+    int best = 1;
+    long best_cost = -1;
+    for (int ns = min_ns; ns <= tiles; ns++) {
+        const int per_block = (tiles + ns - 1) / ns;
+        if (ns > min_ns && (tiles + per_block - 1) / per_block < ns) continue;   // same chunks as fewer splits
+        const long rounds = ((long)base * ns + kComputeUnits - 1) / kComputeUnits;
+        const long cost = rounds * ((per_block + t_streams - 1) / t_streams + 1) + (ns > 1 ? 1 : 0);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = ns;
+        }
+    }
+    return best;
 }
 
 Plan make_plan(const smla_shape* s) {
     Plan p;
-    const int k = s->num_heads / 16;
-    // head groups per workgroup: 4 when the heads allow it, else 3, 2, 1; the
-    // workgroup then has 8 waves (6 for 3 groups) through token-parallel sets
-    p.nhg = k % 4 == 0 ? 4 : k % 3 == 0 ? 3 : k % 2 == 0 ? 2 : 1;
-    if (k == 0) p.nhg = 1;
-    p.tw = p.nhg == 4 || p.nhg == 3 ? 1 : p.nhg == 2 ? 2 : 4;
-    p.n_hg = k == 0 ? 0 : k / p.nhg;
+    const int n_hg = s->num_heads / 16;
+    p.g = n_hg % 4 == 0 ? 4 : n_hg % 2 == 0 ? 2 : 1;
+    p.n_hb = n_hg / p.g;
     const int tiles = (s->topk + kTile - 1) / kTile;
+    // shared-tile workgroups keep their chunk's list entries in LDS
+    const int min_ns = p.g > 1 ? (s->topk + kMaxChunk - 1) / kMaxChunk : 1;
     int ns = s->num_splits;
-    if (ns == 0) {
-        // about one workgroup per compute unit
-        const int base = s->batch * (p.n_hg > 0 ? p.n_hg : 1);
-        ns = base > 0 ? (256 + base - 1) / base : 1;
-    }
-    // the index chunk of a workgroup lives in LDS: at most kMaxChunk entries
-    const int min_ns = (s->topk + kMaxChunk - 1) / kMaxChunk;
+    if (ns == 0) ns = choose_splits(s->batch * p.n_hb, tiles, kWaves / p.g, min_ns > 0 ? min_ns : 1);
     if (ns < min_ns) ns = min_ns;
     if (ns > tiles) ns = tiles;
     if (ns < 1) ns = 1;
@@ -613,12 +790,6 @@ smla_status device_check() {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-
-template <int NHG, int TW>
-hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((smla_decode_kernel<NHG, TW>), dim3(grid), dim3(64 * NHG * 2 * TW), 0, st, a);
-    return hipGetLastError();
-}
 
 }  // namespace
 
@@ -691,22 +862,21 @@ static smla_status prepare(const void* q, const void* kv_cache, const int32_t* t
     a->topk = shape->topk;
     a->nsplit = p->nsplit;
     a->chunk = p->chunk;
-    a->n_hg = p->n_hg;
+    a->n_hb = p->n_hb;
+    a->seq_bytes = (uint32_t)(shape->kv_seq_stride * kRowBytes);
     return SMLA_OK;
 }
 
 static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
-    const int grid = a.batch * p.n_hg * p.nsplit;
+    const int grid = a.batch * p.n_hb * p.nsplit;
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    hipError_t e;
-    switch (p.nhg) {
-        case 4: e = launch_decode<4, 1>(args, grid, hs); break;
-        case 3: e = launch_decode<3, 1>(args, grid, hs); break;
-        case 2: e = launch_decode<2, 2>(args, grid, hs); break;
-        default: e = launch_decode<1, 4>(args, grid, hs); break;
+    switch (p.g) {
+        case 4: hipLaunchKernelGGL(smla_decode_kernel<4>, dim3(grid), dim3(64 * kWaves), 0, hs, args); break;
+        case 2: hipLaunchKernelGGL(smla_decode_kernel<2>, dim3(grid), dim3(64 * kWaves), 0, hs, args); break;
+        default: hipLaunchKernelGGL(smla_decode_kernel<1>, dim3(grid), dim3(64 * kWaves), 0, hs, args); break;
     }
-    return e == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
 smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* topk_idx,
