@@ -105,7 +105,7 @@ constexpr int kAccBytes = 32 * 64 * 16;             // one wave's output accumul
 template <int G>
 struct Geo {
     static constexpr int T = kWaves / G;
-    static constexpr int NS = G == 1 ? 2 : G == 2 ? 3 : 7;
+    static constexpr int NS = G == 1 ? 2 : G == 2 ? 3 : 4;
     static constexpr int L = (kRowGathers + kScaleGathers + G - 1) / G;   // shared modes
     static constexpr int kRing = T * NS * kSlot;
     static constexpr int kIdx = kRing;                                   // index table
@@ -343,29 +343,34 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
 
     // ---------------- S^T = K . Q^T per 16-token half; lane group q takes
     // columns 16q..16q+15 of every 64-column group (two K-steps of 8), and rope
-    // columns 16q..16q+15
+    // columns 16q..16q+15.  The K rows of the second half are read before the
+    // first half is converted.
+    u32x4 raw[2][7];
+    u32x4 rr[2][2];
+    auto load_half = [&](int tt) {
+        const uint8_t* krow = st + (16 * tt + ln) * kRowLds;
+#pragma unroll
+        for (int g = 0; g < 7; g++) raw[tt][g] = *(const u32x4*)(krow + 64 * g + 16 * qg);
+        rr[tt][0] = *(const u32x4*)(krow + kLdsRope + 32 * qg);
+        rr[tt][1] = *(const u32x4*)(krow + kLdsRope + 32 * qg + 16);
+    };
+    load_half(0);
+    load_half(1);
     f32x4 s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
-        const uint8_t* krow = st + (16 * tt + ln) * kRowLds;
-        u32x4 raw[7];
-        u32x4 rr[2];
-#pragma unroll
-        for (int g = 0; g < 7; g++) raw[g] = *(const u32x4*)(krow + 64 * g + 16 * qg);
-        rr[0] = *(const u32x4*)(krow + kLdsRope + 32 * qg);
-        rr[1] = *(const u32x4*)(krow + kLdsRope + 32 * qg + 16);
         f32x4 acc[8];
 #pragma unroll
         for (int g = 0; g < 7; g++)
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][0], raw[g][1]), qop[2 * g],
-                                                             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[0]), qop[14], f32x4{0.f, 0.f, 0.f, 0.f},
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[tt][g][0], raw[tt][g][1]),
+                                                             qop[2 * g], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[tt][0]), qop[14], f32x4{0.f, 0.f, 0.f, 0.f},
                                                          0, 0, 0);
 #pragma unroll
         for (int g = 0; g < 7; g++)
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][2], raw[g][3]), qop[2 * g + 1],
-                                                             acc[g], 0, 0, 0);
-        acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[1]), qop[15], acc[7], 0, 0, 0);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[tt][g][2], raw[tt][g][3]),
+                                                             qop[2 * g + 1], acc[g], 0, 0, 0);
+        acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[tt][1]), qop[15], acc[7], 0, 0, 0);
         f32x4 v = acc[7];
 #pragma unroll
         for (int g = 0; g < 7; g++)
@@ -405,41 +410,52 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
     }
 
     // ---------------- O^T += V^T . P^T
-    // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2), byte half j%2
+    // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2),
+    // byte half j%2; rope V^T via tr16, lane 16q + 4r + c supplies
+    // slot_token(8q + r), then slot_token(8q + 4 + r), columns 4c..4c+3 of each
+    // 16-column block.  The reads of group g + 1 are issued before group g is
+    // converted (one wave per SIMD has no other wave to hide LDS latency).
     const uint8_t* tr_row = st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1);
-#pragma unroll
-    for (int g = 0; g < 7; g++) {
-        i32x2 vraw[4];
+    const int col = 8 * (ln & 3);
+    const uint8_t* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col;
+    const uint8_t* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col;
+    i32x2 vraw[2][4];
+    f32x4 svv[2][2];
+    auto load_group = [&](int g, int buf) {
 #pragma unroll
         for (int cb = 0; cb < 4; cb++)
-            vraw[cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * g + 16 * cb));
+            vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * g + 16 * cb));
+        svv[buf][0] = *(const f32x4*)(sT + g * kTile + 4 * qg);
+        svv[buf][1] = *(const f32x4*)(sT + g * kTile + 16 + 4 * qg);
+    };
+    load_group(0, 0);
+    s16x4 rv[4][2];
+#pragma unroll
+    for (int g = 0; g < 7; g++) {
+        const int cur = g & 1;
+        if (g + 1 < 7) load_group(g + 1, cur ^ 1);
+        if (g == 1) {
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                rv[dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
+                rv[dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
+            }
+        }
         // weights fp16(p * scale_g); exact fp8 -> fp16 value codes
-        const f32x4 sv0 = *(const f32x4*)(sT + g * kTile + 4 * qg);
-        const f32x4 sv1 = *(const f32x4*)(sT + g * kTile + 16 + 4 * qg);
         f16x8 bop;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            bop[j] = (_Float16)(p[j] * sv0[j]);
-            bop[4 + j] = (_Float16)(p[4 + j] * sv1[j]);
+            bop[j] = (_Float16)(p[j] * svv[cur][0][j]);
+            bop[4 + j] = (_Float16)(p[4 + j] * svv[cur][1][j]);
         }
 #pragma unroll
         for (int cb = 0; cb < 4; cb++)
             acc_o[4 * g + cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                codes_to_f16((uint32_t)vraw[cb][0], (uint32_t)vraw[cb][1]), bop, acc_o[4 * g + cb], 0, 0, 0);
+                codes_to_f16((uint32_t)vraw[cur][cb][0], (uint32_t)vraw[cur][cb][1]), bop, acc_o[4 * g + cb],
+                0, 0, 0);
     }
     {
-        // rope V^T via tr16: lane 16q + 4r + c supplies slot_token(8q + r), then
-        // slot_token(8q + 4 + r), columns 4c..4c+3 of each 16-column block
-        const int col = 8 * (ln & 3);
-        const uint8_t* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col;
-        const uint8_t* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col;
-        s16x4 rv[4][2];
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-            rv[dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
-            rv[dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
-        }
-        // bf16 values as stored; weights split into bf16 high and low parts
+        // rope: bf16 values as stored; weights split into bf16 high and low parts
         bf16x8 phi, plo;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -666,7 +682,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     }
 }
 
-// Log-sum-exp merge: one wave per (b, h), 8 columns per lane.
+// Log-sum-exp merge: one wave per (b, h), 8 columns per lane.  The split
+// log-sum-exps are wave-uniform (scalar loads); the partial outputs are read
+// four splits at a time with all loads issued before they are used, so every
+// wave keeps eight 16-byte loads in flight.  An empty split (lse = -inf) has
+// weight exp(-inf) = 0 and a zero partial.
 __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, const float* lse_part,
                                                            int32_t rows, int32_t nsplit,
                                                            uint16_t* out, float* lse) {
@@ -676,18 +696,33 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
     const float* lp = lse_part + (int64_t)row * nsplit;
     float M = -INFINITY;
     for (int i = 0; i < nsplit; i++) M = fmaxf(M, lp[i]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    const float* src = o_part + (int64_t)row * nsplit * kLatent + 8 * lane;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     float W = 0.f;
-    if (M != -INFINITY) {
-        for (int i = 0; i < nsplit; i++) {
-            const float li = lp[i];
-            if (li == -INFINITY) continue;
-            const float w = __expf(li - M);
-            W += w;
-            const float* src = o_part + ((int64_t)row * nsplit + i) * kLatent + 8 * lane;
-            acc0 += w * *(const f32x4*)src;
-            acc1 += w * *(const f32x4*)(src + 4);
+    int i = 0;
+    for (; i + 4 <= nsplit; i += 4) {
+        f32x4 lo[4], hi[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            lo[k] = *(const f32x4*)(src + (i + k) * kLatent);
+            hi[k] = *(const f32x4*)(src + (i + k) * kLatent + 4);
         }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float w = __expf(lp[i + k] - Ms);
+            W += w;
+            acc0 += w * lo[k];
+            acc1 += w * hi[k];
+        }
+    }
+    for (; i < nsplit; i++) {
+        const f32x4 lo = *(const f32x4*)(src + i * kLatent);
+        const f32x4 hi = *(const f32x4*)(src + i * kLatent + 4);
+        const float w = __expf(lp[i] - Ms);
+        W += w;
+        acc0 += w * lo;
+        acc1 += w * hi;
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     u32x4 pk;
@@ -745,7 +780,11 @@ int choose_splits(int base, int tiles, int t_streams, int min_ns) {
 Plan make_plan(const smla_shape* s) {
     Plan p;
     const int n_hg = s->num_heads / 16;
-    p.g = n_hg % 4 == 0 ? 4 : n_hg % 2 == 0 ? 2 : 1;
+    // shared tiles pay for themselves once there are enough (sequence, head
+    // block) pairs that few splits fill the chip; otherwise the per-wave mode
+    // keeps the split partials (and the combine) small
+    const int64_t pairs4 = (int64_t)s->batch * (n_hg / 4), pairs2 = (int64_t)s->batch * (n_hg / 2);
+    p.g = n_hg % 4 == 0 && pairs4 >= 64 ? 4 : n_hg % 2 == 0 && pairs2 >= 64 ? 2 : 1;
     p.n_hb = n_hg / p.g;
     const int tiles = (s->topk + kTile - 1) / kTile;
     // shared-tile workgroups keep their chunk's list entries in LDS
