@@ -71,6 +71,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+typedef __attribute__((address_space(3))) const f32x4 lds_cf32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) const float lds_cf32;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef __attribute__((address_space(3))) const int32_t lds_ci32;
 
 // LDS tile slot: 32 rows of codes and rope, row-major, kRowLds bytes apart,
 // followed by the tile's group scales transposed to [group][token].
@@ -167,6 +175,14 @@ __device__ __forceinline__ float lanegroup_sum(float x) {
     const uint32_t v = __float_as_uint(x);
     const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// An LDS address the compiler must treat as opaque: every read of a tile then
+// uses one base register plus immediate offsets, instead of loop-invariant
+// per-offset address registers.
+__device__ __forceinline__ const lds_u8* opaque(const lds_u8* p) {
+    asm volatile("" : "+v"(p));
+    return p;
 }
 
 // Token held in MFMA k-slot `slot` (0..31) of a 32-token tile.  The S^T
@@ -301,7 +317,7 @@ __device__ __forceinline__ void issue_tile_own(int row_of_lane, i32x4 rsrc, uint
 // LDS index table; live = false gathers zeros.  The table lookups are all
 // issued before the first gather.
 template <int G, int L>
-__device__ __forceinline__ void issue_tile_shared(const int32_t* rows, bool live, i32x4 rsrc, uint32_t slot_lds,
+__device__ __forceinline__ void issue_tile_shared(lds_ci32* rows, bool live, i32x4 rsrc, uint32_t slot_lds,
                                                   uint32_t dummy_lds, int hgl, int lane) {
     int row[L];
 #pragma unroll
@@ -333,13 +349,13 @@ __device__ __forceinline__ void issue_tile_shared(const int32_t* rows, bool live
 
 // One 32-token tile for one wave: 16 heads x the full latent.  st is the
 // tile's LDS slot; vmask marks the kept tokens.
-__device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, const bf16x8 (&qop)[16],
+__device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, const bf16x8 (&qop)[16],
                                              f32x4 (&acc_o)[32], float& m_run, float& l_run, int lane,
                                              float logit_factor) {
     const int qg = lane >> 4, ln = lane & 15;
 
     // group scales, transposed: sT[g * 32 + t] = scale g of token t
-    const float* sT = (const float*)(st + kScaleTable);
+    lds_cf32* sT = (lds_cf32*)(st + kScaleTable);
 
     // ---------------- S^T = K . Q^T per 16-token half; lane group q takes
     // columns 16q..16q+15 of every 64-column group (two K-steps of 8), and rope
@@ -348,11 +364,11 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
     u32x4 raw[2][7];
     u32x4 rr[2][2];
     auto load_half = [&](int tt) {
-        const uint8_t* krow = st + (16 * tt + ln) * kRowLds;
+        const lds_u8* krow = st + (16 * tt + ln) * kRowLds;
 #pragma unroll
-        for (int g = 0; g < 7; g++) raw[tt][g] = *(const u32x4*)(krow + 64 * g + 16 * qg);
-        rr[tt][0] = *(const u32x4*)(krow + kLdsRope + 32 * qg);
-        rr[tt][1] = *(const u32x4*)(krow + kLdsRope + 32 * qg + 16);
+        for (int g = 0; g < 7; g++) raw[tt][g] = *(lds_cu32x4*)(krow + 64 * g + 16 * qg);
+        rr[tt][0] = *(lds_cu32x4*)(krow + kLdsRope + 32 * qg);
+        rr[tt][1] = *(lds_cu32x4*)(krow + kLdsRope + 32 * qg + 16);
     };
     load_half(0);
     load_half(1);
@@ -374,7 +390,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
         f32x4 v = acc[7];
 #pragma unroll
         for (int g = 0; g < 7; g++)
-            v += *(const f32x4*)(sT + g * kTile + 16 * tt + 4 * qg) * acc[g];
+            v += *(lds_cf32x4*)(sT + g * kTile + 16 * tt + 4 * qg) * acc[g];
         s[tt] = v;
     }
 #pragma unroll
@@ -415,18 +431,18 @@ __device__ __forceinline__ void compute_tile(const uint8_t* st, uint64_t vmask, 
     // slot_token(8q + r), then slot_token(8q + 4 + r), columns 4c..4c+3 of each
     // 16-column block.  The reads of group g + 1 are issued before group g is
     // converted (one wave per SIMD has no other wave to hide LDS latency).
-    const uint8_t* tr_row = st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1);
+    const lds_u8* tr_row = st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1);
     const int col = 8 * (ln & 3);
-    const uint8_t* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col;
-    const uint8_t* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col;
+    const lds_u8* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col;
+    const lds_u8* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col;
     i32x2 vraw[2][4];
     f32x4 svv[2][2];
     auto load_group = [&](int g, int buf) {
 #pragma unroll
         for (int cb = 0; cb < 4; cb++)
             vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * g + 16 * cb));
-        svv[buf][0] = *(const f32x4*)(sT + g * kTile + 4 * qg);
-        svv[buf][1] = *(const f32x4*)(sT + g * kTile + 16 + 4 * qg);
+        svv[buf][0] = *(lds_cf32x4*)(sT + g * kTile + 4 * qg);
+        svv[buf][1] = *(lds_cf32x4*)(sT + g * kTile + 16 + 4 * qg);
     };
     load_group(0, 0);
     s16x4 rv[4][2];
@@ -492,7 +508,8 @@ template <int G>
 __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs a) {
     using Ge = Geo<G>;
     constexpr int T = Ge::T, NS = Ge::NS;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[Ge::kLds];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[Ge::kLds];
+    lds_u8* const lds = (lds_u8*)lds_raw;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -542,7 +559,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     if constexpr (G == 1) {
         // ---- independent waves: tiles wave, wave + 4, ...; rows one tile ahead
         const int my_n = wave < ntiles ? (ntiles - 1 - wave) / kWaves + 1 : 0;
-        uint8_t* my_lds = lds + wave * NS * kSlot;
+        lds_u8* my_lds = lds + wave * NS * kSlot;
         const uint32_t my_lds_addr = (uint32_t)(uintptr_t)my_lds;
         auto tile_row = [&](int i) -> int {   // sanitised row of token (lane & 31) of tile i
             const int e = (wave + kWaves * i) * kTile + (lane & 31);
@@ -574,7 +591,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         wait_vmcnt<0>();
     } else {
         // ---- shared tiles: sanitised index table, NS-slot ring per stream
-        int32_t* idx_s = (int32_t*)(lds + Ge::kIdx);
+        lds_i32* idx_s = (lds_i32*)(lds + Ge::kIdx);
         for (int i = threadIdx.x; i < ntiles * kTile; i += 64 * kWaves) {
             int row = -1;
             if (i < n_ent) {
@@ -585,13 +602,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         }
         __syncthreads();
         const int nsteps = (ntiles + T - 1) / T;
-        uint8_t* ring = lds + strm * NS * kSlot;
+        lds_u8* ring = lds + strm * NS * kSlot;
         const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
         const uint32_t dummy_addr = (uint32_t)(uintptr_t)(lds + Ge::kDummy);
         auto issue_step = [&](int step) {
             const int tile = strm + T * step;
             const bool live = tile < ntiles;
-            const int32_t* rows = idx_s + (live ? tile : 0) * kTile;
+            lds_ci32* rows = idx_s + (live ? tile : 0) * kTile;
             const uint32_t slot = ring_addr + (step % NS) * kSlot;
             issue_tile_shared<G, Ge::L>(rows, live, rsrc, slot, dummy_addr, hgl, lane);
         };
@@ -623,7 +640,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     float M = m_run, L = l_tot;
     if constexpr (T > 1) {
         __syncthreads();   // every wave is done with the ring (the merge reuses it)
-        float* stat = (float*)(lds + Ge::kStat);   // [wave][max 16 | sum 16]
+        lds_f32* stat = (lds_f32*)(lds + Ge::kStat);   // [wave][max 16 | sum 16]
         if (lane < 16) {
             stat[wave * 32 + lane] = m_run;
             stat[wave * 32 + 16 + lane] = l_tot;
@@ -638,7 +655,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         for (int s2 = 0; s2 < T; s2++)
             L += __builtin_amdgcn_exp2f(stat[(s2 * G + hgl) * 32 + ln] - Ms0) * stat[(s2 * G + hgl) * 32 + 16 + ln];
         const float aw = __builtin_amdgcn_exp2f(m_run - Ms0);
-        f32x4* part = (f32x4*)(lds + wave * kAccBytes);
+        lds_f32x4* part = (lds_f32x4*)(lds + wave * kAccBytes);
 #pragma unroll
         for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i] * aw;
         __syncthreads();
@@ -652,9 +669,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     const bool final_out = a.nsplit == 1 && !a.force_partials;
     auto block_sum = [&](int i) -> f32x4 {
         if constexpr (T > 1) {
-            f32x4 v = ((const f32x4*)(lds + hgl * kAccBytes))[i * 64 + lane];
+            f32x4 v = ((lds_cf32x4*)(lds + hgl * kAccBytes))[i * 64 + lane];
 #pragma unroll
-            for (int s2 = 1; s2 < T; s2++) v += ((const f32x4*)(lds + (s2 * G + hgl) * kAccBytes))[i * 64 + lane];
+            for (int s2 = 1; s2 < T; s2++) v += ((lds_cf32x4*)(lds + (s2 * G + hgl) * kAccBytes))[i * 64 + lane];
             return v;
         } else {
             return acc_o[i];
@@ -679,6 +696,330 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     if (strm == 0 && qg == 0) {
         if (final_out) a.lse[bh] = lse2 * kLn2;
         else a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Shared tiles with the latent split across wave pairs: G = 2 or 4 head
+// groups of 16 heads per workgroup and 2G waves.  Wave 2h + d serves head
+// group h for half d of the latent: d = 0 takes nope groups 0..3 (columns
+// 0..255), d = 1 nope groups 4..6 and the rope (columns 256..511).  Each wave
+// therefore holds half of its heads' query (32 registers) and half of their
+// output accumulator (64 registers), so that two waves share a SIMD and hide
+// each other's latencies.  The two halves of a pair exchange their partial
+// logits through LDS; the loop is software-pipelined so that one workgroup
+// barrier per tile suffices: iteration j finishes tile j - 1 (partner's
+// partial logits, softmax, PV) and starts tile j (QK partial), and the tile
+// slot is refilled two iterations after its QK.
+template <int G>
+struct SplitGeo {
+    static constexpr int W = 2 * G;                                           // waves
+    static constexpr int NS = G == 4 ? 5 : 6;                                 // ring slots
+    static constexpr int L = (kRowGathers + kScaleGathers + W - 1) / W;      // gathers per wave per tile
+    static constexpr int kIdx = NS * kSlot;                                   // index table
+    static constexpr int kDummy = kIdx + kMaxChunk * 4;                       // no-op gather target
+    static constexpr int kXs = kDummy + 1024;                                 // [2][W][64 lanes][8] partial logits
+    static constexpr int kLds = kXs + 2 * W * 64 * 8 * 4;
+    static_assert(kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static_assert(L * W <= kRowGathers + kScaleGathers + 1, "at most one no-op gather per tile");
+    static_assert(NS >= 3, "a slot is read by the QK of one iteration and the PV of the next");
+};
+
+// Partial logits S^T of latent half dh for the 32 tokens of a tile: sp[tt]
+// holds tokens 16tt + 4q + j (j = 0..3) for head ln, summed over the half's
+// units with the group scales applied.  Units 0..2 are nope groups 4dh + u;
+// unit 3 is nope group 3 (dh = 0) or the rope (dh = 1, unscaled).  Both
+// halves run the same instruction stream apart from unit 3.  qh[2u + ks]: the
+// query columns of unit u for K-step ks (8 columns per lane group q:
+// 16q + 8ks.. of the unit's 64 columns).
+__device__ __forceinline__ void qk_half(const lds_u8* st, int dh, const bf16x8 (&qh)[8], int lane, f32x4 (&sp)[2]) {
+    const int qg = lane >> 4, ln = lane & 15;
+    const lds_u8* kbase = opaque(st + ln * kRowLds + 16 * qg + 256 * dh);                // K rows, this half
+    lds_cf32* sT = (lds_cf32*)opaque(st + kScaleTable + 16 * qg + 512 * dh);            // scales of groups 4dh..
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+        const lds_u8* krow = kbase + 16 * tt * kRowLds;
+        u32x4 raw[4];
+        u32x4 rr[2];
+#pragma unroll
+        for (int u = 0; u < 3; u++) raw[u] = *(lds_cu32x4*)(krow + 64 * u);
+        if (dh == 0) {
+            raw[3] = *(lds_cu32x4*)(krow + 64 * 3);
+        } else {
+            // rope columns 16q..16q+15 sit at LDS bytes 448 + 32q of the row (krow is 256 + 16q)
+            rr[0] = *(lds_cu32x4*)(krow + kLdsRope - 256 + 16 * qg);
+            rr[1] = *(lds_cu32x4*)(krow + kLdsRope - 256 + 16 * qg + 16);
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int u = 0; u < 3; u++)
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[u][0], raw[u][1]), qh[2 * u],
+                                                             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 3; u++)
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[u][2], raw[u][3]), qh[2 * u + 1],
+                                                             acc[u], 0, 0, 0);
+        f32x4 v;
+        if (dh == 0) {
+            acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[3][0], raw[3][1]), qh[6],
+                                                             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[3][2], raw[3][3]), qh[7], acc[3],
+                                                             0, 0, 0);
+            v = *(lds_cf32x4*)(sT + 3 * kTile + 16 * tt) * acc[3];
+        } else {
+            v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[0]), qh[6], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[1]), qh[7], v, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 3; u++) v += *(lds_cf32x4*)(sT + u * kTile + 16 * tt) * acc[u];
+        sp[tt] = v;
+    }
+}
+
+// Online softmax (log2 domain, lazy rescale) of one tile's logits s (tokens
+// 16tt + 4q + j for head ln); masked tokens get -inf.  Returns the weights in
+// k-slot order (tokens 4q+j, then 16+4q+j) and rescales acc when the base moves.
+template <int NACC>
+__device__ __forceinline__ void softmax_tile(f32x4 (&s)[2], uint64_t vmask, float logit_factor, int lane,
+                                             f32x4 (&acc)[NACC], float& m_run, float& l_run, float (&p)[8]) {
+    const int qg = lane >> 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float z = s[tt][j] * logit_factor;
+            s[tt][j] = ((vmask >> (16 * tt + 4 * qg + j)) & 1) ? z : -INFINITY;
+        }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = lanegroup_max(mx);
+    const bool need = mx > m_run + kTau;
+    if (__any(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        // the first kept tokens only set the base: the accumulators are still zero
+        if (__any(m_run != -INFINITY)) {
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < NACC; i++) acc[i] *= alpha;
+        }
+        m_run = m_new;
+    }
+    const float base = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        p[j] = __builtin_amdgcn_exp2f(s[j >> 2][j & 3] - base);
+        l_run += p[j];
+    }
+}
+
+// O^T += V^T . P^T over latent half dh's columns: acc[4u + cb] holds unit u,
+// column block cb (units as in qk_half: nope groups 4dh + u, and unit 3 =
+// nope group 3 or the rope).
+__device__ __forceinline__ void pv_half(const lds_u8* st, int dh, const float (&p)[8], int lane, f32x4 (&acc)[16]) {
+    const int qg = lane >> 4, ln = lane & 15;
+    lds_cf32* sT = (lds_cf32*)opaque(st + kScaleTable + 16 * qg + 512 * dh);
+    // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2),
+    // byte half j%2; the reads of unit u + 1 are issued before unit u is converted
+    const lds_u8* tr_row = opaque(st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1) + 256 * dh);
+    const int nnope = dh == 0 ? 4 : 3;   // nope units of this half
+    i32x2 vraw[2][4];
+    f32x4 sv[2][2];
+    auto load_unit = [&](int u, int buf) {
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++)
+            vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * u + 16 * cb));
+        sv[buf][0] = *(lds_cf32x4*)(sT + u * kTile);
+        sv[buf][1] = *(lds_cf32x4*)(sT + u * kTile + 16);
+    };
+    load_unit(0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int cur = u & 1;
+        if (u == 3 && nnope == 3) break;
+        if (u + 1 < 3 || (u + 1 == 3 && nnope == 4)) load_unit(u + 1, cur ^ 1);
+        // weights fp16(p * scale_g); exact fp8 -> fp16 value codes
+        f16x8 bop;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            bop[j] = (_Float16)(p[j] * sv[cur][0][j]);
+            bop[4 + j] = (_Float16)(p[4 + j] * sv[cur][1][j]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++)
+            acc[4 * u + cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                codes_to_f16((uint32_t)vraw[cur][cb][0], (uint32_t)vraw[cur][cb][1]), bop, acc[4 * u + cb], 0, 0, 0);
+    }
+    if (dh == 1) {
+        // rope V^T via tr16: lane 16q + 4r + c supplies slot_token(8q + r), then
+        // slot_token(8q + 4 + r), columns 4c..4c+3 of each 16-column block; bf16
+        // values as stored, weights split into bf16 high and low parts
+        const int col = 8 * (ln & 3);
+        const lds_u8* r0 = opaque(st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col);
+        const lds_u8* r1 = opaque(st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col);
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const __bf16 h = (__bf16)p[j];
+            phi[j] = h;
+            plo[j] = (__bf16)(p[j] - (float)h);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            s16x4 rv[2];
+            rv[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
+            rv[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
+            bf16x8 aop;
+            memcpy(&aop, rv, 16);
+            f32x4 c = acc[12 + dt];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, c, 0, 0, 0);
+            acc[12 + dt] = c;
+        }
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void split_loop(const DecodeArgs& a, lds_u8* lds, int wave, int dh, int lane, int ntiles,
+                                           lds_ci32* idx_s, i32x4 rsrc, const bf16x8 (&qh_in)[8],
+                                           f32x4 (&acc)[16], float& m_run, float& l_run) {
+    using Ge = SplitGeo<G>;
+    constexpr int W = Ge::W, NS = Ge::NS, L = Ge::L;
+    bf16x8 qh[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) qh[k] = qh_in[k];
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)lds;
+    const uint32_t dummy_addr = (uint32_t)(uintptr_t)(lds + Ge::kDummy);
+    lds_f32* xs = (lds_f32*)(lds + Ge::kXs);   // [buf][wave][lane][8]
+    const int partner = wave ^ 1;
+    auto issue = [&](int t) {
+        const bool live = t < ntiles;
+        issue_tile_shared<W, L>(idx_s + (live ? t : 0) * kTile, live, rsrc, ring_addr + (t % NS) * kSlot,
+                                dummy_addr, wave, lane);
+    };
+#pragma unroll
+    for (int t = 1; t < NS - 2; t++) issue(t);
+    f32x4 sp[2];
+    for (int j = 0; j <= ntiles; j++) {
+        wait_vmcnt<(NS - 3) * L>();   // this wave's gathers of tile j have landed
+        lds_barrier();                // ... and everyone's; tile j - 2's slot and xs[j & 1] are free
+        issue(j + NS - 2);
+        float p[8];
+        if (j >= 1) {
+            // logits of tile j - 1: both halves, summed in the same order in both waves
+            lds_cf32* xo = xs + (((j - 1) & 1) * W + partner) * 512 + 8 * lane;
+            const f32x4 o0 = *(lds_cf32x4*)xo;
+            const f32x4 o1 = *(lds_cf32x4*)(xo + 4);
+            f32x4 s[2];
+            s[0] = dh == 0 ? sp[0] + o0 : o0 + sp[0];
+            s[1] = dh == 0 ? sp[1] + o1 : o1 + sp[1];
+            const uint64_t vmask = __ballot(lane < kTile && idx_s[(j - 1) * kTile + (lane & 31)] >= 0);
+            softmax_tile<16>(s, vmask, a.logit_factor, lane, acc, m_run, l_run, p);
+        }
+        if (j >= 1) pv_half(lds + ((j - 1) % NS) * kSlot, dh, p, lane, acc);
+        __builtin_amdgcn_sched_barrier(0);   // register budget: PV's operands die before QK's are read
+        if (j < ntiles) {
+            qk_half(lds + (j % NS) * kSlot, dh, qh, lane, sp);
+            lds_f32* xm = xs + ((j & 1) * W + wave) * 512 + 8 * lane;
+            *(lds_f32x4*)xm = sp[0];
+            *(lds_f32x4*)(xm + 4) = sp[1];
+        }
+    }
+    wait_vmcnt<0>();   // trailing no-op loads of the ring
+}
+
+template <int G>
+__global__ __launch_bounds__(128 * G, 1) void smla_decode_split_kernel(DecodeArgs a) {
+    using Ge = SplitGeo<G>;
+    constexpr int W = Ge::W;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[Ge::kLds];
+    lds_u8* const lds = (lds_u8*)lds_raw;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qg = lane >> 4;
+    const int ln = lane & 15;
+    const int dh = wave & 1;                   // latent half
+    const int hgl = wave >> 1;                 // head group within the workgroup
+
+    int bid = blockIdx.x;
+    if (a.xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+    const int split = bid % a.nsplit;
+    bid /= a.nsplit;
+    const int hb = bid % a.n_hb;
+    const int b = bid / a.n_hb;
+
+    const int head = 16 * (G * hb + hgl) + ln;
+    const int t_begin = split * a.chunk;
+    const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
+    const int ntiles = (n_ent + kTile - 1) / kTile;
+    const int seqlen = a.seqlens[b];
+    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * kRowBytes, a.seq_bytes);
+    const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
+
+    // ---- sanitised index table of the split's chunk
+    lds_i32* idx_s = (lds_i32*)(lds + Ge::kIdx);
+    for (int i = threadIdx.x; i < ntiles * kTile; i += 64 * W) {
+        int row = -1;
+        if (i < n_ent) {
+            row = idx_b[i];
+            if (row < 0 || row >= seqlen) row = -1;
+        }
+        idx_s[i] = row;
+    }
+    __syncthreads();
+    {
+        const bool live = ntiles > 0;
+        issue_tile_shared<W, Ge::L>(idx_s, live, rsrc, (uint32_t)(uintptr_t)lds,
+                                    (uint32_t)(uintptr_t)(lds + Ge::kDummy), wave, lane);
+    }
+
+    // ---- this half of the query as the B operand of S^T = K . Q^T (k-slot
+    // order matches the K reads: lane group q takes columns 16q..16q+15 of
+    // every 64-column group, 8 per K-step, and rope columns 16q..16q+15)
+    bf16x8 qh[8];
+    {
+        // units 0..2: nope groups 4dh + u; unit 3: nope group 3 (dh = 0) or the rope
+        const uint16_t* qrow = a.q + ((int64_t)b * a.heads + head) * kLatent;
+        const uint16_t* qhalf = qrow + 256 * dh;
+#pragma unroll
+        for (int u = 0; u < 3; u++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+                qh[2 * u + ks] = as_bf16x8(*(const u32x4*)(qhalf + 64 * u + 16 * qg + 8 * ks));
+        const uint16_t* q3 = dh == 0 ? qrow + 64 * 3 : qrow + kNope;
+        qh[6] = as_bf16x8(*(const u32x4*)(q3 + 16 * qg));
+        qh[7] = as_bf16x8(*(const u32x4*)(q3 + 16 * qg + 8));
+    }
+    f32x4 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the query must have landed before the tile loop (one wait, here)
+#pragma unroll
+    for (int k = 0; k < 8; k++) asm volatile("" : "+v"(qh[k]));
+    float m_run = -INFINITY, l_run = 0.f;
+    split_loop<G>(a, lds, wave, dh, lane, ntiles, idx_s, rsrc, qh, acc, m_run, l_run);
+
+    // ---- this half of the split's output: block i holds columns 256 dh + 16i + 4qg + j
+    const float L = lanegroup_sum(l_run);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float lse2 = L > 0.f ? m_run + log2f(L) : -INFINITY;
+    const int64_t bh = (int64_t)b * a.heads + head;
+    if (a.nsplit == 1 && !a.force_partials) {
+        uint16_t* o = a.out + bh * kLatent + 256 * dh + 4 * qg;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+            w[1] = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+            *(u32x2*)(o + 16 * i) = w;
+        }
+        if (dh == 0 && qg == 0) a.lse[bh] = lse2 * kLn2;
+    } else {
+        float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 256 * dh + 4 * qg;
+#pragma unroll
+        for (int i = 0; i < 16; i++) *(f32x4*)(o + 16 * i) = acc[i] * inv;
+        if (dh == 0 && qg == 0) a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
     }
 }
 
@@ -911,8 +1252,8 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     switch (p.g) {
-        case 4: hipLaunchKernelGGL(smla_decode_kernel<4>, dim3(grid), dim3(64 * kWaves), 0, hs, args); break;
-        case 2: hipLaunchKernelGGL(smla_decode_kernel<2>, dim3(grid), dim3(64 * kWaves), 0, hs, args); break;
+        case 4: hipLaunchKernelGGL(smla_decode_split_kernel<4>, dim3(grid), dim3(128 * 4), 0, hs, args); break;
+        case 2: hipLaunchKernelGGL(smla_decode_split_kernel<2>, dim3(grid), dim3(128 * 2), 0, hs, args); break;
         default: hipLaunchKernelGGL(smla_decode_kernel<1>, dim3(grid), dim3(64 * kWaves), 0, hs, args); break;
     }
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
