@@ -17,9 +17,9 @@
 //  * 448 = 7 groups x 64 columns = 14 MFMA K-steps of 32: no padding at all.
 //  * Every wave is an independent decoder for 16 heads over the full 512-wide
 //    latent: it owns two 32-token LDS slots, gathers its next tile straight
-//    into one (global_load_lds, 16 bytes per lane, coalesced along the row)
-//    while it computes the current one from the other, and never waits for
-//    another wave until the end.  A workgroup is four such waves (one per
+//    into one (buffer_load_dwordx4 with the lds bit, 16 bytes per lane,
+//    coalesced along the row) while it computes the current one from the
+//    other, and never waits for another wave until the end.  A workgroup is four such waves (one per
 //    SIMD, the whole 160 KB LDS) on the same (sequence, head group, split);
 //    they take the split's tiles round robin and merge their online-softmax
 //    states once, through LDS, at the end.
@@ -82,49 +82,28 @@ typedef __attribute__((address_space(3))) const int32_t lds_ci32;
 
 // LDS tile slot: 32 rows of codes and rope, row-major, kRowLds bytes apart,
 // followed by the tile's group scales transposed to [group][token].
-// LDS row: bytes 0..447 the fp8 codes, 448..575 the rope, 576..591 unused.
-// The pitch of 37 16-byte pieces makes the 16 rows read by one 16-lane group
-// start in 16 distinct 4-bank sets.  The scales arrive by a separate 4-byte
-// gather per (token, group), which writes the transposed table directly.
-constexpr int kPieces = 37;                         // LDS row pitch in 16-byte pieces
+// LDS row: bytes 0..447 the fp8 codes, 448..575 the rope, 576..607 unused.
+// With a pitch of 38 16-byte pieces the 16 rows read by one 16-lane group
+// start in distinct bank sets (a 592-byte pitch costs a 2-way conflict), and
+// 32 rows are exactly 19 gathers of 64 lanes.  The scales arrive by a separate
+// 4-byte gather per (token, group), which writes the transposed table directly.
+constexpr int kPieces = 38;                         // LDS row pitch in 16-byte pieces
 constexpr int kCodePieces = 28;                     // pieces 0..27: codes; 28..35: rope
-constexpr int kRowLds = kPieces * 16;               // 592
+constexpr int kRowLds = kPieces * 16;               // 608
 constexpr int kLdsRope = kNope;                     // rope offset inside an LDS row (448)
-constexpr int kScaleTable = kTile * kRowLds;        // scale table offset in a slot (18944)
-constexpr int kSlot = kScaleTable + 8 * kTile * 4;  // 19968 bytes per tile slot
-constexpr int kRowGathers = (kTile * kPieces + 63) / 64;   // 19 row gathers of 64 lanes
+constexpr int kScaleTable = kTile * kRowLds;        // scale table offset in a slot (19456)
+constexpr int kSlot = kScaleTable + 8 * kTile * 4;  // 20480 bytes per tile slot
+constexpr int kRowGathers = kTile * kPieces / 64;   // 19 row gathers of 64 lanes
 constexpr int kScaleGathers = 4;                    // 4-byte gathers of the scale table
 constexpr int kWaves = 4;                           // waves per workgroup (one per SIMD)
-constexpr int kMaxChunk = 2048;                     // list entries of a shared-tile workgroup
 constexpr int kAccBytes = 32 * 64 * 16;             // one wave's output accumulator (32 KB)
+constexpr int kWaveLds = 2 * kSlot;                 // two tile slots per wave
+constexpr int kStat = kWaves * kAccBytes;           // merge statistics, after the merge buffers
+constexpr int kLdsBytes = kWaves * kWaveLds;        // the whole 160 KB
 
-// Workgroup geometry for G head groups of 16 heads per workgroup (G = 1, 2, 4).
-// The four waves form T = 4 / G tile streams; stream s takes tiles s, s + T,
-// ... of the workgroup's chunk, and its G waves (one per head group) share
-// each of its tiles.  A stream owns a ring of NS tile slots.
-//  * G = 1: every wave is its own stream with two slots; it loads the rows of
-//    its next tile into registers one tile ahead and issues all gathers of a
-//    tile itself; no wave ever waits for another before the merge.
-//  * G = 2, 4: the chunk's (sanitised) list entries sit in an LDS table, every
-//    wave issues L of the tile's 23 gathers (one more, a no-op load, pads the
-//    count so that all waves count the same loads per tile), NS - 1 tiles are
-//    in flight, and a workgroup barrier per tile step recycles the slot of the
-//    previous step.
-template <int G>
-struct Geo {
-    static constexpr int T = kWaves / G;
-    static constexpr int NS = G == 1 ? 2 : G == 2 ? 3 : 4;
-    static constexpr int L = (kRowGathers + kScaleGathers + G - 1) / G;   // shared modes
-    static constexpr int kRing = T * NS * kSlot;
-    static constexpr int kIdx = kRing;                                   // index table
-    static constexpr int kDummy = kIdx + (G > 1 ? kMaxChunk * 4 : 0);    // no-op gather target
-    static constexpr int kEnd = kDummy + (G > 1 ? 1024 : 0);
-    static constexpr int kMerge = T > 1 ? kWaves * kAccBytes : 0;        // reuses the ring
-    static constexpr int kStat = kEnd > kMerge ? kEnd : kMerge;          // per-wave (max, sum)
-    static constexpr int kLds = kStat + kWaves * 32 * 4;
-    static_assert(kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-    static_assert(G == 1 || L * G <= kRowGathers + kScaleGathers + 1, "at most one no-op gather per tile");
-};
+static_assert(kTile * kPieces % 64 == 0, "whole row gathers");
+static_assert(kStat + kWaves * 32 * 4 <= kLdsBytes, "merge buffers and statistics reuse the slots");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 
 __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -208,9 +187,9 @@ __device__ __forceinline__ i32x4 row_rsrc(const uint8_t* base, uint32_t bytes) {
     return r;
 }
 
-// Byte offset of 16-byte piece `off` of cache row `row` (row in [-1, 2^23)).
-__device__ __forceinline__ uint32_t row_offset(int row, int off) {
-    return (uint32_t)(__mul24(row, kRowBytes) + off);
+// Byte offset of byte `off` of cache row `row` (row in [-1, 2^23)), modulo 2^32.
+__device__ __forceinline__ uint32_t row_offset(int row, uint32_t off) {
+    return (uint32_t)__mul24(row, kRowBytes) + off;
 }
 
 // 16-byte (4-byte) gather of one lane straight into LDS at lds_base + 16 *
@@ -266,32 +245,32 @@ struct DecodeArgs {
 };
 
 // Source byte offset inside a cache row of LDS piece p: pieces 0..27 are the
-// codes, 28..35 the rope (cache pieces 30..37), 36 the unused pitch padding
-// (cache piece 38).
-__device__ __forceinline__ int piece_src(int p) { return 16 * (p < kCodePieces ? p : p + 2); }
+// codes, 28..35 the rope (cache pieces 30..37).  Pieces 36 and 37 are the
+// pitch padding: bit 31 is added to their offsets, which puts them out of
+// range for every row including the masked row -1 (a sequence's rows end below
+// 2^31 - 128), so the hardware skips those loads and writes zeros.
+__device__ __forceinline__ uint32_t piece_src(int p) {
+    return (16u * p + ((uint32_t)(p >= kCodePieces) << 5)) | ((uint32_t)(p >= kPieces - 2) << 31);
+}
 
-// G = 1: gather one whole 32-token tile into the LDS slot at slot_lds.  Every
-// lane holds the (sanitised) row of token (lane & 31).  Row gather k covers
-// the slot's bytes [1024k, 1024k + 1024): lane l loads LDS piece p = c % 37 of
-// token r = c / 37 (c = 64k + l), whose row comes from lane r by ds_bpermute.
+// Gather one whole 32-token tile into the LDS slot at slot_lds.  Every lane
+// holds the (sanitised) row of token (lane & 31).  Row gather k covers the
+// slot's bytes [1024k, 1024k + 1024): lane l loads LDS piece p = c % 38 of
+// token r = c / 38 (c = 64k + l), whose row comes from lane r by ds_bpermute.
 // Scale gather k' loads scale 2k' + (l >> 5) of token l & 31 into the table.
 __device__ __forceinline__ void issue_tile_own(int row_of_lane, i32x4 rsrc, uint32_t slot_lds, int lane_in) {
     int lane = lane_in;
     asm volatile("" : "+v"(lane));   // keep the per-lane piece walk inside the loop (registers)
-    int r = 0;
-    int p = lane;
-    if (p >= kPieces) {
-        p -= kPieces;
-        r = 1;
-    }
+    int r = lane >= kPieces ? 1 : 0;
+    int p = lane - kPieces * r;
     int rows[kRowGathers];
-    int offs[kRowGathers];
+    uint32_t offs[kRowGathers];
 #pragma unroll
     for (int k = 0; k < kRowGathers; k++) {
         rows[k] = __builtin_amdgcn_ds_bpermute(4 * (r & 31), row_of_lane);
         offs[k] = piece_src(p);
-        // next piece: c + 64 = c + 37 + 27
-        p += 27;
+        // next piece: c + 64 = c + 38 + 26
+        p += 26;
         r += 1;
         if (p >= kPieces) {
             p -= kPieces;
@@ -306,45 +285,7 @@ __device__ __forceinline__ void issue_tile_own(int row_of_lane, i32x4 rsrc, uint
         gather4(row_offset(row_of_lane, SMLA_SCALE_OFFSET + 4 * (2 * k + (lane >> 5))), rsrc,
                 slot_lds + kScaleTable + 256 * k);
 #pragma unroll
-    for (int k = 0; k < kRowGathers; k++)
-        if (k + 1 < kRowGathers || lane < kTile * kPieces - 64 * (kRowGathers - 1))
-            gather16(row_offset(rows[k], offs[k]), rsrc, slot_lds + 1024 * k);
-}
-
-// G = 2, 4: this wave's gathers of a tile are ids hgl, hgl + G, ... (L of
-// them): 0..18 row gathers, 19..22 scale gathers, anything else a no-op load
-// of zeros into the dummy area.  rows points at the tile's 32 entries of the
-// LDS index table; live = false gathers zeros.  The table lookups are all
-// issued before the first gather.
-template <int G, int L>
-__device__ __forceinline__ void issue_tile_shared(lds_ci32* rows, bool live, i32x4 rsrc, uint32_t slot_lds,
-                                                  uint32_t dummy_lds, int hgl, int lane) {
-    int row[L];
-#pragma unroll
-    for (int u = 0; u < L; u++) {
-        const int id = hgl + G * u;
-        const int c = 64 * id + lane;
-        const int r = id < kRowGathers ? (c * 1772) >> 16 : lane;   // c / 37 for c < 1216
-        row[u] = rows[r & 31];
-    }
-#pragma unroll
-    for (int u = 0; u < L; u++) asm volatile("" : "+v"(row[u]));
-#pragma unroll
-    for (int u = 0; u < L; u++) {
-        const int id = hgl + G * u;
-        const int rw = live ? row[u] : -1;
-        if (id < kRowGathers) {
-            const int c = 64 * id + lane;
-            const int p = c - kPieces * ((c * 1772) >> 16);
-            if (c < kTile * kPieces) gather16(row_offset(rw, piece_src(p)), rsrc, slot_lds + 1024 * id);
-        } else if (id < kRowGathers + kScaleGathers) {
-            const int k = id - kRowGathers;
-            gather4(row_offset(rw, SMLA_SCALE_OFFSET + 4 * (2 * k + (lane >> 5))), rsrc,
-                    slot_lds + kScaleTable + 256 * k);
-        } else {
-            gather4(0x80000000u, rsrc, dummy_lds);
-        }
-    }
+    for (int k = 0; k < kRowGathers; k++) gather16(row_offset(rows[k], offs[k]), rsrc, slot_lds + 1024 * k);
 }
 
 // One 32-token tile for one wave: 16 heads x the full latent.  st is the
@@ -500,23 +441,19 @@ __device__ __forceinline__ void pin_state(bf16x8 (&qop)[16], f32x4 (&acc_o)[32])
     for (int k = 0; k < 32; k++) asm volatile("" : "+a"(acc_o[k]));
 }
 
-// One workgroup = (sequence b, head block hb of G x 16 heads, split); see Geo
-// for how its four waves share the split's tiles.  At the end the T streams'
-// states of each head group are merged through LDS and the workgroup writes
-// the split's normalised output and log-sum-exp (or the final bf16 result).
-template <int G>
+// One workgroup = (sequence b, block hb of 16 heads, split).  Its four waves
+// decode the split's tiles independently (wave w takes tiles w, w + 4, ...,
+// each gathered into the wave's own two LDS slots one tile ahead), then merge
+// their online-softmax states once, through LDS, and write the split's
+// normalised output and log-sum-exp (or the final bf16 result).
 __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs a) {
-    using Ge = Geo<G>;
-    constexpr int T = Ge::T, NS = Ge::NS;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[Ge::kLds];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
     lds_u8* const lds = (lds_u8*)lds_raw;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qg = lane >> 4;                  // lane group 0..3
     const int ln = lane & 15;                  // head column of the 16x16 tiles
-    const int strm = wave / G;                 // tile stream
-    const int hgl = wave % G;                  // head group within the workgroup
 
     int bid = blockIdx.x;
     if (a.xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
@@ -525,7 +462,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     const int hb = bid % a.n_hb;
     const int b = bid / a.n_hb;
 
-    const int head = 16 * (G * hb + hgl) + ln;
+    const int head = 16 * hb + ln;
     const int t_begin = split * a.chunk;
     const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
     const int ntiles = (n_ent + kTile - 1) / kTile;
@@ -556,132 +493,78 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     float m_run = -INFINITY;   // base of the exponentials for this lane's head (log2 units)
     float l_run = 0.f;         // partial sum of weights over this lane's tokens
 
-    if constexpr (G == 1) {
-        // ---- independent waves: tiles wave, wave + 4, ...; rows one tile ahead
-        const int my_n = wave < ntiles ? (ntiles - 1 - wave) / kWaves + 1 : 0;
-        lds_u8* my_lds = lds + wave * NS * kSlot;
-        const uint32_t my_lds_addr = (uint32_t)(uintptr_t)my_lds;
-        auto tile_row = [&](int i) -> int {   // sanitised row of token (lane & 31) of tile i
-            const int e = (wave + kWaves * i) * kTile + (lane & 31);
-            int row = -1;
-            if (e < n_ent) {
-                row = idx_b[e];
-                if (row < 0 || row >= seqlen) row = -1;
-            }
-            return row;
-        };
-        int row_cur = -1, row_next = -1;
-        if (my_n > 0) {
-            row_cur = tile_row(0);
-            issue_tile_own(row_cur, rsrc, my_lds_addr, lane);
-        }
-        load_query();
-        pin_state(qop, acc_o);
-        if (my_n > 1) row_next = tile_row(1);
-        for (int i = 0; i < my_n; i++) {
-            pin_state(qop, acc_o);
-            wait_vmcnt<0>();   // tile i is in its slot; the rows of tile i + 1 are in registers
-            if (i + 1 < my_n) issue_tile_own(row_next, rsrc, my_lds_addr + ((i + 1) & 1) * kSlot, lane);
-            const int row_after = i + 2 < my_n ? tile_row(i + 2) : -1;
-            const uint64_t vmask = __ballot(lane < kTile && row_cur >= 0);
-            compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor);
-            row_cur = row_next;
-            row_next = row_after;
-        }
-        wait_vmcnt<0>();
-    } else {
-        // ---- shared tiles: sanitised index table, NS-slot ring per stream
-        lds_i32* idx_s = (lds_i32*)(lds + Ge::kIdx);
-        for (int i = threadIdx.x; i < ntiles * kTile; i += 64 * kWaves) {
-            int row = -1;
-            if (i < n_ent) {
-                row = idx_b[i];
-                if (row < 0 || row >= seqlen) row = -1;
-            }
-            idx_s[i] = row;
-        }
-        __syncthreads();
-        const int nsteps = (ntiles + T - 1) / T;
-        lds_u8* ring = lds + strm * NS * kSlot;
-        const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-        const uint32_t dummy_addr = (uint32_t)(uintptr_t)(lds + Ge::kDummy);
-        auto issue_step = [&](int step) {
-            const int tile = strm + T * step;
-            const bool live = tile < ntiles;
-            lds_ci32* rows = idx_s + (live ? tile : 0) * kTile;
-            const uint32_t slot = ring_addr + (step % NS) * kSlot;
-            issue_tile_shared<G, Ge::L>(rows, live, rsrc, slot, dummy_addr, hgl, lane);
-        };
-        issue_step(0);
-        load_query();
-        pin_state(qop, acc_o);
-#pragma unroll
-        for (int st = 1; st < NS - 1; st++) issue_step(st);
-        // at least one step even for an empty split (it computes a zero-filled
-        // slot with no kept token), so the accumulators have a single path
-        int step = 0;
-        do {
-            pin_state(qop, acc_o);
-            wait_vmcnt<(NS - 2) * Ge::L>();   // this wave's gathers of this step's tile have landed
-            lds_barrier();                    // ... and everyone's; the previous step's slot is free
-            issue_step(step + NS - 1);
-            // a stream past the end of the chunk (G = 2, last step) computes its
-            // zero-filled slot with no kept token, which changes nothing
-            const int tile = strm + T * step;
-            const bool live = tile < ntiles;
-            const uint64_t vmask = __ballot(live && lane < kTile && idx_s[(live ? tile : 0) * kTile + (lane & 31)] >= 0);
-            compute_tile(ring + (step % NS) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor);
-        } while (++step < nsteps);
-        wait_vmcnt<0>();   // trailing no-op loads of the ring
+    // ---- tiles wave, wave + 4, ...  The list entries of tile i + 2 are loaded
+    // while tile i is computed and checked only after the next wait for the
+    // gathers (a check right after the load would make that wait cover the
+    // gathers just issued and stall on them).
+    const int my_n = wave < ntiles ? (ntiles - 1 - wave) / kWaves + 1 : 0;
+    lds_u8* my_lds = lds + wave * kWaveLds;
+    const uint32_t my_lds_addr = (uint32_t)(uintptr_t)my_lds;
+    auto entry = [&](int i) { return (wave + kWaves * i) * kTile + (lane & 31); };
+    // list entry of token (lane & 31) of tile i < my_n (clamped into the chunk)
+    auto load_entry = [&](int i) -> int { return idx_b[min(entry(i), n_ent - 1)]; };
+    // the row it selects, or -1 for a masked entry (past the list, negative,
+    // or not below the sequence length)
+    auto sanitise = [&](int i, int v) -> int { return entry(i) < n_ent && v >= 0 && v < seqlen ? v : -1; };
+    int row_cur = -1, ent_next = -1;
+    if (my_n > 0) {
+        row_cur = sanitise(0, load_entry(0));
+        issue_tile_own(row_cur, rsrc, my_lds_addr, lane);
     }
+    load_query();
+    pin_state(qop, acc_o);
+    if (my_n > 1) ent_next = load_entry(1);
+    for (int i = 0; i < my_n; i++) {
+        pin_state(qop, acc_o);
+        wait_vmcnt<0>();   // tile i is in its slot; the entries of tile i + 1 are in registers
+        const int row_next = sanitise(i + 1, ent_next);
+        if (i + 1 < my_n) issue_tile_own(row_next, rsrc, my_lds_addr + ((i + 1) & 1) * kSlot, lane);
+        ent_next = load_entry(min(i + 2, my_n - 1));
+        const uint64_t vmask = __ballot(lane < kTile && row_cur >= 0);
+        compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor);
+        row_cur = row_next;
+    }
+    wait_vmcnt<0>();
 
-    // ---------------- merge of the T streams of each head group
+    // ---------------- merge of the four waves' states
     const float l_tot = lanegroup_sum(l_run);
-    float M = m_run, L = l_tot;
-    if constexpr (T > 1) {
-        __syncthreads();   // every wave is done with the ring (the merge reuses it)
-        lds_f32* stat = (lds_f32*)(lds + Ge::kStat);   // [wave][max 16 | sum 16]
-        if (lane < 16) {
-            stat[wave * 32 + lane] = m_run;
-            stat[wave * 32 + 16 + lane] = l_tot;
-        }
-        __syncthreads();
-        M = -INFINITY;
-#pragma unroll
-        for (int s2 = 0; s2 < T; s2++) M = fmaxf(M, stat[(s2 * G + hgl) * 32 + ln]);
-        const float Ms0 = M == -INFINITY ? 0.f : M;
-        L = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < T; s2++)
-            L += __builtin_amdgcn_exp2f(stat[(s2 * G + hgl) * 32 + ln] - Ms0) * stat[(s2 * G + hgl) * 32 + 16 + ln];
-        const float aw = __builtin_amdgcn_exp2f(m_run - Ms0);
-        lds_f32x4* part = (lds_f32x4*)(lds + wave * kAccBytes);
-#pragma unroll
-        for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i] * aw;
-        __syncthreads();
+    __syncthreads();   // every wave is done with its slots (the merge reuses them)
+    lds_f32* stat = (lds_f32*)(lds + kStat);   // [wave][max 16 | sum 16]
+    if (lane < 16) {
+        stat[wave * 32 + lane] = m_run;
+        stat[wave * 32 + 16 + lane] = l_tot;
     }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, stat[w * 32 + ln]);
+    const float Ms0 = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) L += __builtin_amdgcn_exp2f(stat[w * 32 + ln] - Ms0) * stat[w * 32 + 16 + ln];
+    const float aw = __builtin_amdgcn_exp2f(m_run - Ms0);
+    lds_f32x4* part = (lds_f32x4*)(lds + wave * kAccBytes);
+#pragma unroll
+    for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i] * aw;
+    __syncthreads();
 
-    // stream s finishes accumulator blocks [s * 32 / T, (s + 1) * 32 / T) of its
-    // head group; block i holds columns 16i + 4qg + j for head ln
+    // wave w finishes accumulator blocks 8w..8w+7; block i holds columns
+    // 16i + 4qg + j for head ln
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const float lse2 = L > 0.f ? M + log2f(L) : -INFINITY;
     const int64_t bh = (int64_t)b * a.heads + head;
     const bool final_out = a.nsplit == 1 && !a.force_partials;
     auto block_sum = [&](int i) -> f32x4 {
-        if constexpr (T > 1) {
-            f32x4 v = ((lds_cf32x4*)(lds + hgl * kAccBytes))[i * 64 + lane];
+        f32x4 v = ((lds_cf32x4*)lds)[i * 64 + lane];
 #pragma unroll
-            for (int s2 = 1; s2 < T; s2++) v += ((lds_cf32x4*)(lds + (s2 * G + hgl) * kAccBytes))[i * 64 + lane];
-            return v;
-        } else {
-            return acc_o[i];
-        }
+        for (int w = 1; w < kWaves; w++) v += ((lds_cf32x4*)(lds + w * kAccBytes))[i * 64 + lane];
+        return v;
     };
-    const int i0 = T == 1 ? 0 : strm * (32 / T);   // static index when T == 1
+    const int i0 = wave * (32 / kWaves);
     if (final_out) {
         uint16_t* o = a.out + bh * kLatent + 4 * qg;
 #pragma unroll
-        for (int ii = 0; ii < 32 / T; ii++) {
+        for (int ii = 0; ii < 32 / kWaves; ii++) {
             const f32x4 v = block_sum(i0 + ii);
             u32x2 w;
             w[0] = pack_bf16x2(v[0] * inv, v[1] * inv);
@@ -691,335 +574,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     } else {
         float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 4 * qg;
 #pragma unroll
-        for (int ii = 0; ii < 32 / T; ii++) *(f32x4*)(o + 16 * (i0 + ii)) = block_sum(i0 + ii) * inv;
+        for (int ii = 0; ii < 32 / kWaves; ii++) *(f32x4*)(o + 16 * (i0 + ii)) = block_sum(i0 + ii) * inv;
     }
-    if (strm == 0 && qg == 0) {
+    if (wave == 0 && qg == 0) {
         if (final_out) a.lse[bh] = lse2 * kLn2;
         else a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Shared tiles with the latent split across wave pairs: G = 2 or 4 head
-// groups of 16 heads per workgroup and 2G waves.  Wave 2h + d serves head
-// group h for half d of the latent: d = 0 takes nope groups 0..3 (columns
-// 0..255), d = 1 nope groups 4..6 and the rope (columns 256..511).  Each wave
-// therefore holds half of its heads' query (32 registers) and half of their
-// output accumulator (64 registers), so that two waves share a SIMD and hide
-// each other's latencies.  The two halves of a pair exchange their partial
-// logits through LDS; the loop is software-pipelined so that one workgroup
-// barrier per tile suffices: iteration j finishes tile j - 1 (partner's
-// partial logits, softmax, PV) and starts tile j (QK partial), and the tile
-// slot is refilled two iterations after its QK.
-template <int G>
-struct SplitGeo {
-    static constexpr int W = 2 * G;                                           // waves
-    static constexpr int NS = G == 4 ? 5 : 6;                                 // ring slots
-    static constexpr int L = (kRowGathers + kScaleGathers + W - 1) / W;      // gathers per wave per tile
-    static constexpr int kIdx = NS * kSlot;                                   // index table
-    static constexpr int kDummy = kIdx + kMaxChunk * 4;                       // no-op gather target
-    static constexpr int kXs = kDummy + 1024;                                 // [2][W][64 lanes][8] partial logits
-    static constexpr int kLds = kXs + 2 * W * 64 * 8 * 4;
-    static_assert(kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-    static_assert(L * W <= kRowGathers + kScaleGathers + 1, "at most one no-op gather per tile");
-    static_assert(NS >= 3, "a slot is read by the QK of one iteration and the PV of the next");
-};
-
-// Partial logits S^T of latent half dh for the 32 tokens of a tile: sp[tt]
-// holds tokens 16tt + 4q + j (j = 0..3) for head ln, summed over the half's
-// units with the group scales applied.  Units 0..2 are nope groups 4dh + u;
-// unit 3 is nope group 3 (dh = 0) or the rope (dh = 1, unscaled).  Both
-// halves run the same instruction stream apart from unit 3.  qh[2u + ks]: the
-// query columns of unit u for K-step ks (8 columns per lane group q:
-// 16q + 8ks.. of the unit's 64 columns).
-__device__ __forceinline__ void qk_half(const lds_u8* st, int dh, const bf16x8 (&qh)[8], int lane, f32x4 (&sp)[2]) {
-    const int qg = lane >> 4, ln = lane & 15;
-    const lds_u8* kbase = opaque(st + ln * kRowLds + 16 * qg + 256 * dh);                // K rows, this half
-    lds_cf32* sT = (lds_cf32*)opaque(st + kScaleTable + 16 * qg + 512 * dh);            // scales of groups 4dh..
-#pragma unroll
-    for (int tt = 0; tt < 2; tt++) {
-        const lds_u8* krow = kbase + 16 * tt * kRowLds;
-        u32x4 raw[4];
-        u32x4 rr[2];
-#pragma unroll
-        for (int u = 0; u < 3; u++) raw[u] = *(lds_cu32x4*)(krow + 64 * u);
-        if (dh == 0) {
-            raw[3] = *(lds_cu32x4*)(krow + 64 * 3);
-        } else {
-            // rope columns 16q..16q+15 sit at LDS bytes 448 + 32q of the row (krow is 256 + 16q)
-            rr[0] = *(lds_cu32x4*)(krow + kLdsRope - 256 + 16 * qg);
-            rr[1] = *(lds_cu32x4*)(krow + kLdsRope - 256 + 16 * qg + 16);
-        }
-        f32x4 acc[4];
-#pragma unroll
-        for (int u = 0; u < 3; u++)
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[u][0], raw[u][1]), qh[2 * u],
-                                                             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 3; u++)
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[u][2], raw[u][3]), qh[2 * u + 1],
-                                                             acc[u], 0, 0, 0);
-        f32x4 v;
-        if (dh == 0) {
-            acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[3][0], raw[3][1]), qh[6],
-                                                             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[3][2], raw[3][3]), qh[7], acc[3],
-                                                             0, 0, 0);
-            v = *(lds_cf32x4*)(sT + 3 * kTile + 16 * tt) * acc[3];
-        } else {
-            v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[0]), qh[6], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[1]), qh[7], v, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < 3; u++) v += *(lds_cf32x4*)(sT + u * kTile + 16 * tt) * acc[u];
-        sp[tt] = v;
-    }
-}
-
-// Online softmax (log2 domain, lazy rescale) of one tile's logits s (tokens
-// 16tt + 4q + j for head ln); masked tokens get -inf.  Returns the weights in
-// k-slot order (tokens 4q+j, then 16+4q+j) and rescales acc when the base moves.
-template <int NACC>
-__device__ __forceinline__ void softmax_tile(f32x4 (&s)[2], uint64_t vmask, float logit_factor, int lane,
-                                             f32x4 (&acc)[NACC], float& m_run, float& l_run, float (&p)[8]) {
-    const int qg = lane >> 4;
-#pragma unroll
-    for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float z = s[tt][j] * logit_factor;
-            s[tt][j] = ((vmask >> (16 * tt + 4 * qg + j)) & 1) ? z : -INFINITY;
-        }
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = lanegroup_max(mx);
-    const bool need = mx > m_run + kTau;
-    if (__any(need)) {
-        const float m_new = need ? mx : m_run;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        // the first kept tokens only set the base: the accumulators are still zero
-        if (__any(m_run != -INFINITY)) {
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < NACC; i++) acc[i] *= alpha;
-        }
-        m_run = m_new;
-    }
-    const float base = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        p[j] = __builtin_amdgcn_exp2f(s[j >> 2][j & 3] - base);
-        l_run += p[j];
-    }
-}
-
-// O^T += V^T . P^T over latent half dh's columns: acc[4u + cb] holds unit u,
-// column block cb (units as in qk_half: nope groups 4dh + u, and unit 3 =
-// nope group 3 or the rope).
-__device__ __forceinline__ void pv_half(const lds_u8* st, int dh, const float (&p)[8], int lane, f32x4 (&acc)[16]) {
-    const int qg = lane >> 4, ln = lane & 15;
-    lds_cf32* sT = (lds_cf32*)opaque(st + kScaleTable + 16 * qg + 512 * dh);
-    // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2),
-    // byte half j%2; the reads of unit u + 1 are issued before unit u is converted
-    const lds_u8* tr_row = opaque(st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1) + 256 * dh);
-    const int nnope = dh == 0 ? 4 : 3;   // nope units of this half
-    i32x2 vraw[2][4];
-    f32x4 sv[2][2];
-    auto load_unit = [&](int u, int buf) {
-#pragma unroll
-        for (int cb = 0; cb < 4; cb++)
-            vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * u + 16 * cb));
-        sv[buf][0] = *(lds_cf32x4*)(sT + u * kTile);
-        sv[buf][1] = *(lds_cf32x4*)(sT + u * kTile + 16);
-    };
-    load_unit(0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-        const int cur = u & 1;
-        if (u == 3 && nnope == 3) break;
-        if (u + 1 < 3 || (u + 1 == 3 && nnope == 4)) load_unit(u + 1, cur ^ 1);
-        // weights fp16(p * scale_g); exact fp8 -> fp16 value codes
-        f16x8 bop;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            bop[j] = (_Float16)(p[j] * sv[cur][0][j]);
-            bop[4 + j] = (_Float16)(p[4 + j] * sv[cur][1][j]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; cb++)
-            acc[4 * u + cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                codes_to_f16((uint32_t)vraw[cur][cb][0], (uint32_t)vraw[cur][cb][1]), bop, acc[4 * u + cb], 0, 0, 0);
-    }
-    if (dh == 1) {
-        // rope V^T via tr16: lane 16q + 4r + c supplies slot_token(8q + r), then
-        // slot_token(8q + 4 + r), columns 4c..4c+3 of each 16-column block; bf16
-        // values as stored, weights split into bf16 high and low parts
-        const int col = 8 * (ln & 3);
-        const lds_u8* r0 = opaque(st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col);
-        const lds_u8* r1 = opaque(st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col);
-        bf16x8 phi, plo;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const __bf16 h = (__bf16)p[j];
-            phi[j] = h;
-            plo[j] = (__bf16)(p[j] - (float)h);
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-            s16x4 rv[2];
-            rv[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
-            rv[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
-            bf16x8 aop;
-            memcpy(&aop, rv, 16);
-            f32x4 c = acc[12 + dt];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, c, 0, 0, 0);
-            acc[12 + dt] = c;
-        }
-    }
-}
-
-template <int G>
-__device__ __forceinline__ void split_loop(const DecodeArgs& a, lds_u8* lds, int wave, int dh, int lane, int ntiles,
-                                           lds_ci32* idx_s, i32x4 rsrc, const bf16x8 (&qh_in)[8],
-                                           f32x4 (&acc)[16], float& m_run, float& l_run) {
-    using Ge = SplitGeo<G>;
-    constexpr int W = Ge::W, NS = Ge::NS, L = Ge::L;
-    bf16x8 qh[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) qh[k] = qh_in[k];
-    const uint32_t ring_addr = (uint32_t)(uintptr_t)lds;
-    const uint32_t dummy_addr = (uint32_t)(uintptr_t)(lds + Ge::kDummy);
-    lds_f32* xs = (lds_f32*)(lds + Ge::kXs);   // [buf][wave][lane][8]
-    const int partner = wave ^ 1;
-    auto issue = [&](int t) {
-        const bool live = t < ntiles;
-        issue_tile_shared<W, L>(idx_s + (live ? t : 0) * kTile, live, rsrc, ring_addr + (t % NS) * kSlot,
-                                dummy_addr, wave, lane);
-    };
-#pragma unroll
-    for (int t = 1; t < NS - 2; t++) issue(t);
-    f32x4 sp[2];
-    for (int j = 0; j <= ntiles; j++) {
-        wait_vmcnt<(NS - 3) * L>();   // this wave's gathers of tile j have landed
-        lds_barrier();                // ... and everyone's; tile j - 2's slot and xs[j & 1] are free
-        issue(j + NS - 2);
-        float p[8];
-        if (j >= 1) {
-            // logits of tile j - 1: both halves, summed in the same order in both waves
-            lds_cf32* xo = xs + (((j - 1) & 1) * W + partner) * 512 + 8 * lane;
-            const f32x4 o0 = *(lds_cf32x4*)xo;
-            const f32x4 o1 = *(lds_cf32x4*)(xo + 4);
-            f32x4 s[2];
-            s[0] = dh == 0 ? sp[0] + o0 : o0 + sp[0];
-            s[1] = dh == 0 ? sp[1] + o1 : o1 + sp[1];
-            const uint64_t vmask = __ballot(lane < kTile && idx_s[(j - 1) * kTile + (lane & 31)] >= 0);
-            softmax_tile<16>(s, vmask, a.logit_factor, lane, acc, m_run, l_run, p);
-        }
-        if (j >= 1) pv_half(lds + ((j - 1) % NS) * kSlot, dh, p, lane, acc);
-        __builtin_amdgcn_sched_barrier(0);   // register budget: PV's operands die before QK's are read
-        if (j < ntiles) {
-            qk_half(lds + (j % NS) * kSlot, dh, qh, lane, sp);
-            lds_f32* xm = xs + ((j & 1) * W + wave) * 512 + 8 * lane;
-            *(lds_f32x4*)xm = sp[0];
-            *(lds_f32x4*)(xm + 4) = sp[1];
-        }
-    }
-    wait_vmcnt<0>();   // trailing no-op loads of the ring
-}
-
-template <int G>
-__global__ __launch_bounds__(128 * G, 1) void smla_decode_split_kernel(DecodeArgs a) {
-    using Ge = SplitGeo<G>;
-    constexpr int W = Ge::W;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[Ge::kLds];
-    lds_u8* const lds = (lds_u8*)lds_raw;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int qg = lane >> 4;
-    const int ln = lane & 15;
-    const int dh = wave & 1;                   // latent half
-    const int hgl = wave >> 1;                 // head group within the workgroup
-
-    int bid = blockIdx.x;
-    if (a.xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-    const int split = bid % a.nsplit;
-    bid /= a.nsplit;
-    const int hb = bid % a.n_hb;
-    const int b = bid / a.n_hb;
-
-    const int head = 16 * (G * hb + hgl) + ln;
-    const int t_begin = split * a.chunk;
-    const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
-    const int ntiles = (n_ent + kTile - 1) / kTile;
-    const int seqlen = a.seqlens[b];
-    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * kRowBytes, a.seq_bytes);
-    const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
-
-    // ---- sanitised index table of the split's chunk
-    lds_i32* idx_s = (lds_i32*)(lds + Ge::kIdx);
-    for (int i = threadIdx.x; i < ntiles * kTile; i += 64 * W) {
-        int row = -1;
-        if (i < n_ent) {
-            row = idx_b[i];
-            if (row < 0 || row >= seqlen) row = -1;
-        }
-        idx_s[i] = row;
-    }
-    __syncthreads();
-    {
-        const bool live = ntiles > 0;
-        issue_tile_shared<W, Ge::L>(idx_s, live, rsrc, (uint32_t)(uintptr_t)lds,
-                                    (uint32_t)(uintptr_t)(lds + Ge::kDummy), wave, lane);
-    }
-
-    // ---- this half of the query as the B operand of S^T = K . Q^T (k-slot
-    // order matches the K reads: lane group q takes columns 16q..16q+15 of
-    // every 64-column group, 8 per K-step, and rope columns 16q..16q+15)
-    bf16x8 qh[8];
-    {
-        // units 0..2: nope groups 4dh + u; unit 3: nope group 3 (dh = 0) or the rope
-        const uint16_t* qrow = a.q + ((int64_t)b * a.heads + head) * kLatent;
-        const uint16_t* qhalf = qrow + 256 * dh;
-#pragma unroll
-        for (int u = 0; u < 3; u++)
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++)
-                qh[2 * u + ks] = as_bf16x8(*(const u32x4*)(qhalf + 64 * u + 16 * qg + 8 * ks));
-        const uint16_t* q3 = dh == 0 ? qrow + 64 * 3 : qrow + kNope;
-        qh[6] = as_bf16x8(*(const u32x4*)(q3 + 16 * qg));
-        qh[7] = as_bf16x8(*(const u32x4*)(q3 + 16 * qg + 8));
-    }
-    f32x4 acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // the query must have landed before the tile loop (one wait, here)
-#pragma unroll
-    for (int k = 0; k < 8; k++) asm volatile("" : "+v"(qh[k]));
-    float m_run = -INFINITY, l_run = 0.f;
-    split_loop<G>(a, lds, wave, dh, lane, ntiles, idx_s, rsrc, qh, acc, m_run, l_run);
-
-    // ---- this half of the split's output: block i holds columns 256 dh + 16i + 4qg + j
-    const float L = lanegroup_sum(l_run);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const float lse2 = L > 0.f ? m_run + log2f(L) : -INFINITY;
-    const int64_t bh = (int64_t)b * a.heads + head;
-    if (a.nsplit == 1 && !a.force_partials) {
-        uint16_t* o = a.out + bh * kLatent + 256 * dh + 4 * qg;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            u32x2 w;
-            w[0] = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
-            w[1] = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
-            *(u32x2*)(o + 16 * i) = w;
-        }
-        if (dh == 0 && qg == 0) a.lse[bh] = lse2 * kLn2;
-    } else {
-        float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 256 * dh + 4 * qg;
-#pragma unroll
-        for (int i = 0; i < 16; i++) *(f32x4*)(o + 16 * i) = acc[i] * inv;
-        if (dh == 0 && qg == 0) a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
     }
 }
 
@@ -1079,8 +638,7 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
 // host side
 
 struct Plan {
-    int g;        // 16-head groups per workgroup (1, 2 or 4)
-    int n_hb;     // head blocks (workgroups per sequence and split)
+    int n_hb;     // 16-head blocks (workgroups per sequence and split)
     int nsplit;
     int chunk;    // list entries per split (multiple of kTile)
 };
@@ -1097,19 +655,18 @@ bool shape_ok(const smla_shape* s) {
 constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
 
 // Split count when the caller leaves it to the library.  A workgroup's time is
-// taken as (tile steps + 1) tile times, where a step is T tiles of the split
-// (T = 4 / g), a launch as that times the number of rounds of kComputeUnits
-// workgroups, and any split adds one tile time for the partials and the
-// combine.  Ties go to fewer splits.  min_ns bounds the split size from below.
-int choose_splits(int base, int tiles, int t_streams, int min_ns) {
+// taken as (tiles per wave + 1) tile times, a launch as that times the number
+// of rounds of kComputeUnits workgroups, and any split adds one tile time for
+// the partials and the combine.  Ties go to fewer splits.
+int choose_splits(int base, int tiles) {
     if (base <= 0 || tiles <= 1) return 1;
     int best = 1;
     long best_cost = -1;
-    for (int ns = min_ns; ns <= tiles; ns++) {
+    for (int ns = 1; ns <= tiles; ns++) {
         const int per_block = (tiles + ns - 1) / ns;
-        if (ns > min_ns && (tiles + per_block - 1) / per_block < ns) continue;   // same chunks as fewer splits
+        if (ns > 1 && (tiles + per_block - 1) / per_block < ns) continue;   // same chunks as fewer splits
         const long rounds = ((long)base * ns + kComputeUnits - 1) / kComputeUnits;
-        const long cost = rounds * ((per_block + t_streams - 1) / t_streams + 1) + (ns > 1 ? 1 : 0);
+        const long cost = rounds * ((per_block + kWaves - 1) / kWaves + 1) + (ns > 1 ? 1 : 0);
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
             best = ns;
@@ -1120,19 +677,10 @@ int choose_splits(int base, int tiles, int t_streams, int min_ns) {
 
 Plan make_plan(const smla_shape* s) {
     Plan p;
-    const int n_hg = s->num_heads / 16;
-    // shared tiles pay for themselves once there are enough (sequence, head
-    // block) pairs that few splits fill the chip; otherwise the per-wave mode
-    // keeps the split partials (and the combine) small
-    const int64_t pairs4 = (int64_t)s->batch * (n_hg / 4), pairs2 = (int64_t)s->batch * (n_hg / 2);
-    p.g = n_hg % 4 == 0 && pairs4 >= 64 ? 4 : n_hg % 2 == 0 && pairs2 >= 64 ? 2 : 1;
-    p.n_hb = n_hg / p.g;
+    p.n_hb = s->num_heads / 16;
     const int tiles = (s->topk + kTile - 1) / kTile;
-    // shared-tile workgroups keep their chunk's list entries in LDS
-    const int min_ns = p.g > 1 ? (s->topk + kMaxChunk - 1) / kMaxChunk : 1;
     int ns = s->num_splits;
-    if (ns == 0) ns = choose_splits(s->batch * p.n_hb, tiles, kWaves / p.g, min_ns > 0 ? min_ns : 1);
-    if (ns < min_ns) ns = min_ns;
+    if (ns == 0) ns = choose_splits(s->batch * p.n_hb, tiles);
     if (ns > tiles) ns = tiles;
     if (ns < 1) ns = 1;
     const int per = (s->topk + ns - 1) / ns;
@@ -1251,11 +799,7 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const int grid = a.batch * p.n_hb * p.nsplit;
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    switch (p.g) {
-        case 4: hipLaunchKernelGGL(smla_decode_split_kernel<4>, dim3(grid), dim3(128 * 4), 0, hs, args); break;
-        case 2: hipLaunchKernelGGL(smla_decode_split_kernel<2>, dim3(grid), dim3(128 * 2), 0, hs, args); break;
-        default: hipLaunchKernelGGL(smla_decode_kernel<1>, dim3(grid), dim3(64 * kWaves), 0, hs, args); break;
-    }
+    hipLaunchKernelGGL(smla_decode_kernel, dim3(grid), dim3(64 * kWaves), 0, hs, args);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
