@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of one sparse MLA decode step on one MI355X (gfx950).
 
-A step is the whole hot path over one batch: the split-K decode kernel and,
-when the list is split, the log-sum-exp combine kernel, both in libsmla.so.
+A step is the whole hot path over one batch: one sparse_mla_decode call of
+libsmla.so, i.e. the split-K decode kernel and, when the list is split, the
+log-sum-exp combine kernel.
 Default workload: 32 query tokens x 64 heads, 512 of 32768 cache rows per
 sequence (synthetic, seeded).
 
@@ -10,8 +11,9 @@ Inputs are resident in HBM before timing starts.  To keep each step reading
 HBM rather than the 256 MB last-level cache, the timed loop rotates over R
 copies of the inputs (distinct buffers, same contents) whose total footprint
 exceeds 768 MB.  Warmup steps run first, untimed.  The timed region of K steps
-is bracketed by synchronisations; HIP events on the launch stream time the
-whole loop and every decode and combine launch inside it.
+is bracketed by synchronisations; HIP events on the launch stream at both ends
+time the whole loop.  A second timed loop of K decode-kernel launches alone
+gives that kernel's average duration for the roofline.
 
 Prints one JSON line with queries*heads/s, effective KV GB/s, the roofline
 object of the decode kernel (algorithmic KV bytes = 604 per kept row), and
@@ -21,9 +23,11 @@ the fp64 CPU oracle timed on the host as a baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -40,6 +44,27 @@ ROW_ALGO_BYTES = 604            # 448 fp8 + 7 fp32 scales + 64 bf16 rope per kep
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "decode_b32_h64_s32768_k512_kernel_stats.txt")
+COUNTER_CONFIG = 3
+
+
+def counted_traffic(config):
+    """HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    plain device copy) from the committed rocprofv3 counter summary, when that
+    summary was taken on this workload and on the current kernel source; None
+    otherwise."""
+    if config != COUNTER_CONFIG or not os.path.exists(COUNTER_SUMMARY):
+        return None
+    text = open(COUNTER_SUMMARY).read()
+    src = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc", "smla.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    m_src = re.search(r"sha256\[:16\] = ([0-9a-f]{16})", text)
+    m_dec = re.search(r"decode kernel: FETCH_SIZE .*?-> ([0-9.]+) MB per launch; WRITE_SIZE .*?-> ([0-9.]+) MB", text)
+    if not m_src or not m_dec or m_src.group(1) != digest:
+        return None
+    return (float(m_dec.group(1)) + float(m_dec.group(2))) * 1e6
 
 
 def parse():
@@ -136,6 +161,11 @@ def main():
                           ctypes.byref(shape), P(ws) if ws is not None else None, ctypes.c_size_t(need_ws), hs))
     comb_args = (P(o_part), P(lse_part), B, H, ns, P(out), P(lse), hs)
 
+    def step(i):
+        """One whole step: decode kernel, then the combine kernel when split."""
+        st = L.sparse_mla_decode(*full_args[i % R])
+        assert st == 0, st
+
     def decode_only(i):
         """The decode kernel alone (split partials when the list is split)."""
         if ns == 1:
@@ -143,13 +173,6 @@ def main():
         else:
             st = L.sparse_mla_decode_partials(*dec_args[i % R])
         assert st == 0, st
-
-    def step(i):
-        """One whole step: decode kernel, then the combine kernel when split."""
-        decode_only(i)
-        if ns > 1:
-            st = L.sparse_mla_combine(*comb_args)
-            assert st == 0, st
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -231,7 +254,7 @@ def main():
                    "num_splits": ns, "split_size": chunk, "rotation": R,
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": counted_traffic(args.config)},
         "cpu_baseline": cpu,
         "effective_kv_gbps": kv_gbps,
         "all_algorithmic_gbps": all_bytes / t_dec / 1e9,
@@ -240,8 +263,8 @@ def main():
         "mfma_tflops": flops / t_dec / 1e12,
         "mfma_frac": flops / t_dec / 1e12 / BF16_PEAK_TFLOPS,
         "precision": "fp8 e4m3fn + bf16 KV; QK bf16 MFMA, PV fp16 MFMA, fp32 accumulate; bf16 out",
-        "timing": "HIP events on the launch stream around K back-to-back launches; inputs rotated "
-                  "over R HBM-resident copies",
+        "timing": "HIP events on the launch stream around K back-to-back steps, then around K "
+                  "decode-kernel launches alone; inputs rotated over R HBM-resident copies",
     }
     print(json.dumps(res), flush=True)
 

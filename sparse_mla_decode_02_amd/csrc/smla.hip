@@ -46,6 +46,7 @@
 #include <stdint.h>
 #include <string.h>
 
+
 #include "../../include/smla.h"
 
 namespace {
@@ -441,6 +442,62 @@ __device__ __forceinline__ void pin_state(bf16x8 (&qop)[16], f32x4 (&acc_o)[32])
     for (int k = 0; k < 32; k++) asm volatile("" : "+a"(acc_o[k]));
 }
 
+// Log-sum-exp merge of the split partials of one (b, h) row by one wave, 8
+// columns per lane.  The partial outputs are read four splits at a time with
+// all loads issued before they are used.  An empty split (lse = -inf) has
+// weight exp(-inf) = 0 and a zero partial.
+__device__ __forceinline__ void combine_row(const float* o_part, const float* lse_part, int64_t row,
+                                            int nsplit, uint16_t* out, float* lse, int lane) {
+    const float* lp = lse_part + row * nsplit;
+    float M = -INFINITY;
+    for (int i = 0; i < nsplit; i++) M = fmaxf(M, lp[i]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    const float* src = o_part + row * nsplit * kLatent + 8 * lane;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    int i = 0;
+    for (; i + 4 <= nsplit; i += 4) {
+        f32x4 lo[4], hi[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            lo[k] = *(const f32x4*)(src + (i + k) * kLatent);
+            hi[k] = *(const f32x4*)(src + (i + k) * kLatent + 4);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float w = __expf(lp[i + k] - Ms);
+            W += w;
+            acc0 += w * lo[k];
+            acc1 += w * hi[k];
+        }
+    }
+    for (; i < nsplit; i++) {
+        const f32x4 lo = *(const f32x4*)(src + i * kLatent);
+        const f32x4 hi = *(const f32x4*)(src + i * kLatent + 4);
+        const float w = __expf(lp[i] - Ms);
+        W += w;
+        acc0 += w * lo;
+        acc1 += w * hi;
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    u32x4 pk;
+    pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+    pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+    pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+    pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
+    *(u32x4*)(out + row * kLatent + 8 * lane) = pk;
+    if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
+}
+
+// The combine as its own kernel: one wave per (b, h).
+__global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, const float* lse_part,
+                                                           int32_t rows, int32_t nsplit,
+                                                           uint16_t* out, float* lse) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    combine_row(o_part, lse_part, row, nsplit, out, lse, threadIdx.x & 63);
+}
+
 // One workgroup = (sequence b, block hb of 16 heads, split).  Its four waves
 // decode the split's tiles independently (wave w takes tiles w, w + 4, ...,
 // each gathered into the wave's own two LDS slots one tile ahead), then merge
@@ -508,12 +565,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     auto sanitise = [&](int i, int v) -> int { return entry(i) < n_ent && v >= 0 && v < seqlen ? v : -1; };
     int row_cur = -1, ent_next = -1;
     if (my_n > 0) {
-        row_cur = sanitise(0, load_entry(0));
+        const int ent0 = load_entry(0);
+        ent_next = load_entry(min(1, my_n - 1));
+        row_cur = sanitise(0, ent0);
         issue_tile_own(row_cur, rsrc, my_lds_addr, lane);
     }
     load_query();
     pin_state(qop, acc_o);
-    if (my_n > 1) ent_next = load_entry(1);
     for (int i = 0; i < my_n; i++) {
         pin_state(qop, acc_o);
         wait_vmcnt<0>();   // tile i is in its slot; the entries of tile i + 1 are in registers
@@ -582,61 +640,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     }
 }
 
-// Log-sum-exp merge: one wave per (b, h), 8 columns per lane.  The split
-// log-sum-exps are wave-uniform (scalar loads); the partial outputs are read
-// four splits at a time with all loads issued before they are used, so every
-// wave keeps eight 16-byte loads in flight.  An empty split (lse = -inf) has
-// weight exp(-inf) = 0 and a zero partial.
-__global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, const float* lse_part,
-                                                           int32_t rows, int32_t nsplit,
-                                                           uint16_t* out, float* lse) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const int lane = threadIdx.x & 63;
-    const float* lp = lse_part + (int64_t)row * nsplit;
-    float M = -INFINITY;
-    for (int i = 0; i < nsplit; i++) M = fmaxf(M, lp[i]);
-    const float Ms = M == -INFINITY ? 0.f : M;
-    const float* src = o_part + (int64_t)row * nsplit * kLatent + 8 * lane;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    float W = 0.f;
-    int i = 0;
-    for (; i + 4 <= nsplit; i += 4) {
-        f32x4 lo[4], hi[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            lo[k] = *(const f32x4*)(src + (i + k) * kLatent);
-            hi[k] = *(const f32x4*)(src + (i + k) * kLatent + 4);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const float w = __expf(lp[i + k] - Ms);
-            W += w;
-            acc0 += w * lo[k];
-            acc1 += w * hi[k];
-        }
-    }
-    for (; i < nsplit; i++) {
-        const f32x4 lo = *(const f32x4*)(src + i * kLatent);
-        const f32x4 hi = *(const f32x4*)(src + i * kLatent + 4);
-        const float w = __expf(lp[i] - Ms);
-        W += w;
-        acc0 += w * lo;
-        acc1 += w * hi;
-    }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    u32x4 pk;
-    pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
-    pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
-    pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
-    pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
-    *(u32x4*)(out + (int64_t)row * kLatent + 8 * lane) = pk;
-    if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
-}
-
-// ---------------------------------------------------------------------------
-// host side
-
 struct Plan {
     int n_hb;     // 16-head blocks (workgroups per sequence and split)
     int nsplit;
@@ -653,6 +656,7 @@ bool shape_ok(const smla_shape* s) {
 }
 
 constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
+constexpr int kMaxSplits = 4096;     // bound on the split count
 
 // Split count when the caller leaves it to the library.  A workgroup's time is
 // taken as (tiles per wave + 1) tile times, a launch as that times the number
@@ -682,6 +686,7 @@ Plan make_plan(const smla_shape* s) {
     int ns = s->num_splits;
     if (ns == 0) ns = choose_splits(s->batch * p.n_hb, tiles);
     if (ns > tiles) ns = tiles;
+    if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
     const int per = (s->topk + ns - 1) / ns;
     p.chunk = ((per + kTile - 1) / kTile) * kTile;
@@ -691,13 +696,23 @@ Plan make_plan(const smla_shape* s) {
     return p;
 }
 
-size_t workspace_for(const smla_shape* s, const Plan& p) {
-    if (p.nsplit <= 1) return 0;
+// Workspace of a split launch: o_part fp32 [B][H][S][512], then lse_part fp32
+// [B][H][S], each 256-byte aligned.
+struct WorkspaceLayout {
+    size_t lse_off, bytes;
+};
+
+WorkspaceLayout workspace_layout(const smla_shape* s, const Plan& p) {
+    WorkspaceLayout w = {0, 0};
+    if (p.nsplit <= 1) return w;
     const size_t rows = (size_t)s->batch * s->num_heads * p.nsplit;
-    size_t o_bytes = rows * kLatent * sizeof(float);
-    o_bytes = (o_bytes + 255) & ~(size_t)255;
-    return o_bytes + ((rows * sizeof(float) + 255) & ~(size_t)255);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    w.lse_off = up(rows * kLatent * sizeof(float));
+    w.bytes = w.lse_off + up(rows * sizeof(float));
+    return w;
 }
+
+size_t workspace_for(const smla_shape* s, const Plan& p) { return workspace_layout(s, p).bytes; }
 
 smla_status device_check() {
     int dev = -1;
@@ -824,9 +839,9 @@ smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t
     a.out = (uint16_t*)out;
     a.lse = lse;
     if (p.nsplit > 1) {
-        const size_t rows = (size_t)shape->batch * shape->num_heads * p.nsplit;
+        const WorkspaceLayout w = workspace_layout(shape, p);
         a.o_part = (float*)workspace;
-        a.lse_part = (float*)((char*)workspace + ((rows * kLatent * sizeof(float) + 255) & ~(size_t)255));
+        a.lse_part = (float*)((char*)workspace + w.lse_off);
     }
     hipStream_t hs = (hipStream_t)stream;
     st = launch(a, p, hs);

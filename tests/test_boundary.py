@@ -51,7 +51,8 @@ def test_split_resolution_and_workspace_size():
     assert smla.num_splits(96, 16, 2048, num_splits=8) == 8
     # workspace: fp32 partials [B,H,S,512] then lse [B,H,S], each 256-byte rounded
     rows = 96 * 16 * 8
-    exp = ((rows * 512 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    up = lambda x: (x + 255) // 256 * 256
+    exp = up(rows * 512 * 4) + up(rows * 4)
     assert smla.workspace_bytes(96, 16, 2048, num_splits=8) == exp
     # heuristic always returns a usable count
     for B, H, k in [(1, 16, 64), (32, 64, 512), (64, 64, 2048), (0, 16, 8), (3, 48, 45), (2, 128, 0)]:

@@ -191,3 +191,78 @@ def test_split_partials_against_oracle_partials(topk, nsplit):
     err = np.abs(o - ref_o)
     assert err.max() <= 1e-2 * max(1.0, np.abs(ref_o).max() / 4), err.max()
     assert np.linalg.norm(o - ref_o) / np.linalg.norm(ref_o) <= 5e-3
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    # one workspace, filled with arbitrary bytes once, serves calls of different
+    # shapes and split counts in a row
+    wa, ra_out, ra_lse = case_small(17, batch=6, heads=32, topk=300, seqlen=4000)
+    wb, rb_out, rb_lse = case_small(18, batch=3, heads=64, topk=512, seqlen=2048)
+    ia, ib = device_inputs(wa), device_inputs(wb)
+    need = max(smla.workspace_bytes(wa.batch, wa.heads, wa.topk, 5, wa.kv_seq_stride),
+               smla.workspace_bytes(wb.batch, wb.heads, wb.topk, 3, wb.kv_seq_stride))
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda:0")
+    for w, inp, ns, r_out, r_lse, tag in [(wa, ia, 5, ra_out, ra_lse, "a5"), (wb, ib, 3, rb_out, rb_lse, "b3"),
+                                          (wa, ia, 2, ra_out, ra_lse, "a2"), (wa, ia, 5, ra_out, ra_lse, "a5'")]:
+        log(f"case: workspace reuse {tag}")
+        q, cache, idx, sl = inp
+        out = torch.full((w.batch, w.heads, 512), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.full((w.batch, w.heads), float("nan"), device="cuda:0")
+        smla.sparse_mla_decode(q, cache, idx, sl, w.scale, out, lse, num_splits=ns,
+                               kv_seq_stride=w.kv_seq_stride, workspace=ws)
+        torch.cuda.synchronize()
+        compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                r_out, r_lse, label=f"workspace reuse {tag}")
+
+
+def test_graph_replays_match_eager():
+    # a captured split launch (decode and combine kernels); replays interleaved
+    # with eager calls on the same workspace must all give the eager result
+    w, _, _ = case_small(19, batch=8, heads=64, topk=512, seqlen=8192)
+    q, cache, idx, sl = device_inputs(w)
+    ns = 4
+    ws = torch.empty(smla.workspace_bytes(w.batch, w.heads, w.topk, ns, w.kv_seq_stride),
+                     dtype=torch.uint8, device="cuda:0")
+    out_e = torch.empty((w.batch, w.heads, 512), dtype=torch.bfloat16, device="cuda:0")
+    lse_e = torch.empty((w.batch, w.heads), device="cuda:0")
+    smla.sparse_mla_decode(q, cache, idx, sl, w.scale, out_e, lse_e, num_splits=ns,
+                           kv_seq_stride=w.kv_seq_stride, workspace=ws)
+    torch.cuda.synchronize()
+    ref = (out_e.clone(), lse_e.clone())
+    out_g = torch.empty_like(out_e)
+    lse_g = torch.empty_like(lse_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            smla.sparse_mla_decode(q, cache, idx, sl, w.scale, out_g, lse_g, num_splits=ns,
+                                   kv_seq_stride=w.kv_seq_stride, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(4):
+        log(f"case: graph replay {r}")
+        out_g.fill_(float("nan"))
+        lse_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref[0]) and torch.equal(lse_g, ref[1]), r
+        if r % 2 == 0:   # an eager call on the same workspace in between
+            smla.sparse_mla_decode(q, cache, idx, sl, w.scale, out_e, lse_e, num_splits=ns,
+                                   kv_seq_stride=w.kv_seq_stride, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out_e, ref[0]) and torch.equal(lse_e, ref[1]), r
+
+
+@pytest.mark.parametrize("batch,heads,nsplit", [(5, 16, 7), (3, 48, 5)])
+def test_many_splits_on_grids_without_xcd_remap(batch, heads, nsplit):
+    # grids that are not a multiple of 8 keep the hardware's round-robin
+    # placement of workgroups on XCDs
+    w, ref_out, ref_lse = case_small(20 + batch, batch=batch, heads=heads, topk=1024, seqlen=6000)
+    grid = batch * (heads // 16) * smla.num_splits(batch, heads, 1024, nsplit, w.kv_seq_stride)
+    assert grid % 8 != 0
+    inputs = device_inputs(w)
+    for rep in range(2):
+        log(f"case: splits without remap B={batch} H={heads} ns={nsplit} rep {rep}")
+        out, lse = run_decode(w, inputs, num_splits=nsplit)
+        compare(out, lse, ref_out, ref_lse, label=f"no-remap B{batch} H{heads} ns{nsplit} #{rep}")
