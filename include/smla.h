@@ -34,7 +34,7 @@ extern "C" {
 /* Cache row format: one token's latent row, SMLA_ROW_BYTES apart.
  *   bytes   0..447  nope, 448 fp8 e4m3fn codes (OCP, largest finite 448)
  *   bytes 448..479  8 fp32 group scales; slot g scales nope columns 64g..64g+63
- *                   for g < 7; slot 7 is padding and is never read
+ *                   for g < 7; slot 7 is padding, its value is never used
  *   bytes 480..607  rope, 64 bf16 values
  *   bytes 608..639  padding, never read
  * Dequantised row: K[i] = e4m3(code[i]) * scale[i / 64] for i < 448,
