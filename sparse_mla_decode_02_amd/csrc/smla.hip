@@ -46,6 +46,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 
 #include "../../include/smla.h"
 
@@ -81,28 +83,29 @@ typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef __attribute__((address_space(3))) const int32_t lds_ci32;
 
-// LDS tile slot: 32 rows of codes and rope, row-major, kRowLds bytes apart,
-// followed by the tile's group scales transposed to [group][token].
-// LDS row: bytes 0..447 the fp8 codes, 448..575 the rope, 576..607 unused.
-// With a pitch of 38 16-byte pieces the 16 rows read by one 16-lane group
-// start in distinct bank sets (a 592-byte pitch costs a 2-way conflict), and
-// 32 rows are exactly 19 gathers of 64 lanes.  The scales arrive by a separate
-// 4-byte gather per (token, group), which writes the transposed table directly.
-constexpr int kPieces = 38;                         // LDS row pitch in 16-byte pieces
-constexpr int kCodePieces = 28;                     // pieces 0..27: codes; 28..35: rope
-constexpr int kRowLds = kPieces * 16;               // 608
-constexpr int kLdsRope = kNope;                     // rope offset inside an LDS row (448)
-constexpr int kScaleTable = kTile * kRowLds;        // scale table offset in a slot (19456)
-constexpr int kSlot = kScaleTable + 8 * kTile * 4;  // 20480 bytes per tile slot
-constexpr int kRowGathers = kTile * kPieces / 64;   // 19 row gathers of 64 lanes
-constexpr int kScaleGathers = 4;                    // 4-byte gathers of the scale table
-constexpr int kWaves = 4;                           // waves per workgroup (one per SIMD)
-constexpr int kAccBytes = 32 * 64 * 16;             // one wave's output accumulator (32 KB)
-constexpr int kWaveLds = 2 * kSlot;                 // two tile slots per wave
-constexpr int kStat = kWaves * kAccBytes;           // merge statistics, after the merge buffers
-constexpr int kLdsBytes = kWaves * kWaveLds;        // the whole 160 KB
+// LDS tile slot.  The 36 16-byte pieces of a row (0..27 the fp8 codes, 28..35
+// the rope) are stored in 18 blocks of 1 KB: block 2j + hh holds pieces
+// 4j..4j+3 of the 16 rows in LDS positions 16hh..16hh+15, 64 bytes per row,
+// piece 4j + c of position 16hh + ss at chunk c ^ ((ss >> 2) & 3).  One gather
+// of 64 lanes x 16 bytes fills one block, i.e. 64 contiguous bytes of each of
+// 16 rows (4 rows per quarter-wave: full 64-byte granules), with per-lane
+// source offsets that differ between blocks only by an instruction immediate.
+// The chunk swizzle puts the 16 rows read by one 16-lane group in distinct
+// banks; the position of MFMA token t is lds_pos(t), which does the same for
+// the 8 tokens of one transposed value read.  Then the tile's group scales,
+// transposed to [group][position] (4 bytes each).
+constexpr int kPiecesUsed = 36;                       // 28 code pieces + 8 rope pieces
+constexpr int kCodePieces = 28;
+constexpr int kScaleTable = kPiecesUsed * kTile * 16;  // scale table offset in a slot (18432)
+constexpr int kSlot = kScaleTable + 8 * kTile * 4;    // 19456 bytes per tile slot
+constexpr int kRowGathers = kPiecesUsed / 2;          // 18 row gathers of 64 lanes (one block each)
+constexpr int kScaleGathers = 4;                      // 4-byte gathers of the scale table
+constexpr int kWaves = 4;                             // waves per workgroup (one per SIMD)
+constexpr int kAccBytes = 32 * 64 * 16;               // one wave's output accumulator (32 KB)
+constexpr int kWaveLds = 2 * kSlot;                   // two tile slots per wave
+constexpr int kStat = kWaves * kAccBytes;             // merge statistics, after the merge buffers
+constexpr int kLdsBytes = kWaves * kWaveLds;          // 152 KB
 
-static_assert(kTile * kPieces % 64 == 0, "whole row gathers");
 static_assert(kStat + kWaves * 32 * 4 <= kLdsBytes, "merge buffers and statistics reuse the slots");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 
@@ -173,6 +176,24 @@ __device__ __forceinline__ int slot_token(int slot) {
     return r < 4 ? 4 * q + r : 16 + 4 * q + (r - 4);
 }
 
+// LDS position of MFMA token t (an involution).  Tokens 4q..4q+3 and
+// 16+4q..16+4q+3 (one transposed value read) then sit in positions whose
+// 16-byte chunks fall in distinct banks, and each 16-token half still covers
+// 16 positions with distinct banks.
+__device__ __forceinline__ int lds_pos(int t) { return t ^ ((t & 16) >> 2); }
+
+// Byte offset in a slot of bytes 8h..8h+7 (h = 0, 1) of piece p of the row in
+// LDS position s (see the slot layout above).
+__device__ __forceinline__ int piece_addr(int p, int s, int h = 0) {
+    const int ss = s & 15;
+    return 1024 * (2 * (p >> 2) + (s >> 4)) + 64 * ss + 16 * ((p & 3) ^ ((ss >> 2) & 3)) + 8 * h;
+}
+
+// Valid-token mask in MFMA token order from one in LDS-position order.
+__device__ __forceinline__ uint64_t mask_by_token(uint64_t by_pos) {
+    return (by_pos & 0xFFFFull) | ((by_pos & 0x0F0F0000ull) << 4) | ((by_pos & 0xF0F00000ull) >> 4);
+}
+
 // Buffer resource over one sequence's cache rows (gfx9 raw buffer, stride 0):
 // a gather addresses a row by a 32-bit byte offset, and the hardware range
 // check turns every offset at or past `bytes` into a load of zeros.  A masked
@@ -189,6 +210,7 @@ __device__ __forceinline__ i32x4 row_rsrc(const uint8_t* base, uint32_t bytes) {
 }
 
 // Byte offset of byte `off` of cache row `row` (row in [-1, 2^23)), modulo 2^32.
+// Row -1 gives an offset above 2^32 - 640, out of range for every sequence.
 __device__ __forceinline__ uint32_t row_offset(int row, uint32_t off) {
     return (uint32_t)__mul24(row, kRowBytes) + off;
 }
@@ -211,6 +233,36 @@ __device__ __forceinline__ void gather4(uint32_t voff, i32x4 rsrc, uint32_t lds_
                  :
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory", "m0");
+}
+
+// The same with a constant byte offset kOff (< 4096) in the instruction.  The
+// instruction offset moves the LDS destination as well as the source (checked
+// on gfx950), so M0 is set kOff bytes lower to keep the destination at
+// lds_base (which is at least kOff).
+template <int kOff>
+__device__ __forceinline__ void gather16_at(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
+    static_assert(kOff >= 0 && kOff < 4096, "buffer instruction offset");
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base - kOff)), "n"(kOff)
+                 : "memory", "m0");
+}
+
+template <int kOff>
+__device__ __forceinline__ void gather4_at(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
+    static_assert(kOff >= 0 && kOff < 4096, "buffer instruction offset");
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen offset:%3 lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base - kOff)), "n"(kOff)
+                 : "memory", "m0");
+}
+
+template <int K, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (K < N) {
+        f(std::integral_constant<int, K>{});
+        static_for<K + 1, N>(f);
+    }
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -245,48 +297,46 @@ struct DecodeArgs {
     int32_t xcd_remap;        // grid is a multiple of 8: keep a sequence's blocks on one XCD
 };
 
-// Source byte offset inside a cache row of LDS piece p: pieces 0..27 are the
-// codes, 28..35 the rope (cache pieces 30..37).  Pieces 36 and 37 are the
-// pitch padding: bit 31 is added to their offsets, which puts them out of
-// range for every row including the masked row -1 (a sequence's rows end below
-// 2^31 - 128), so the hardware skips those loads and writes zeros.
-__device__ __forceinline__ uint32_t piece_src(int p) {
-    return (16u * p + ((uint32_t)(p >= kCodePieces) << 5)) | ((uint32_t)(p >= kPieces - 2) << 31);
+// Gather one whole 32-token tile into the LDS slot at slot_lds.  Lane l holds
+// the (sanitised) row of LDS position l & 31.  Block gather 2j + hh: lane l
+// loads the 16 bytes that belong at chunk l & 3 of position 16hh + (l >> 2),
+// i.e. piece 4j + ((l & 3) ^ ((l >> 4) & 3)) of that position's row, from
+// source byte 16 * piece (codes) or 16 * piece + 32 (rope; the scales sit
+// between them in the cache row).  The two rows each lane needs come from the
+// lanes holding them (2 ds_bpermute per tile), and the 18 gathers share two
+// offset registers.  Scale gather k loads scale 2k + (l >> 5) of position
+// l & 31 into row 2k + (l >> 5) of the table; the last one leaves out group 7
+// (padding), whose row holds list entries instead (see load_entries_lds).
+__device__ __forceinline__ void issue_tile(int row, i32x4 rsrc, uint32_t slot_lds, int lane) {
+    const int row0 = __builtin_amdgcn_ds_bpermute(4 * (lane >> 2), row);
+    const int row1 = __builtin_amdgcn_ds_bpermute(4 * (16 + (lane >> 2)), row);
+    const uint32_t pp = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t vscale = row_offset(row, SMLA_SCALE_OFFSET + 4u * ((uint32_t)lane >> 5));
+    static_for<0, kScaleGathers - 1>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        gather4_at<8 * k>(vscale, rsrc, slot_lds + kScaleTable + 256 * k);
+    });
+    if (lane < 32) gather4_at<8 * (kScaleGathers - 1)>(vscale, rsrc, slot_lds + kScaleTable + 256 * (kScaleGathers - 1));
+    const uint32_t v0 = row_offset(row0, 16u * pp);
+    const uint32_t v1 = row_offset(row1, 16u * pp);
+    static_for<0, kRowGathers / 2>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int off = 64 * j + (4 * j >= kCodePieces ? 32 : 0);
+        gather16_at<off>(v0, rsrc, slot_lds + 1024 * (2 * j));
+        gather16_at<off>(v1, rsrc, slot_lds + 1024 * (2 * j + 1));
+    });
 }
 
-// Gather one whole 32-token tile into the LDS slot at slot_lds.  Every lane
-// holds the (sanitised) row of token (lane & 31).  Row gather k covers the
-// slot's bytes [1024k, 1024k + 1024): lane l loads LDS piece p = c % 38 of
-// token r = c / 38 (c = 64k + l), whose row comes from lane r by ds_bpermute.
-// Scale gather k' loads scale 2k' + (l >> 5) of token l & 31 into the table.
-__device__ __forceinline__ void issue_tile_own(int row_of_lane, i32x4 rsrc, uint32_t slot_lds, int lane_in) {
-    int lane = lane_in;
-    asm volatile("" : "+v"(lane));   // keep the per-lane piece walk inside the loop (registers)
-    int r = lane >= kPieces ? 1 : 0;
-    int p = lane - kPieces * r;
-    int rows[kRowGathers];
-    uint32_t offs[kRowGathers];
-#pragma unroll
-    for (int k = 0; k < kRowGathers; k++) {
-        rows[k] = __builtin_amdgcn_ds_bpermute(4 * (r & 31), row_of_lane);
-        offs[k] = piece_src(p);
-        // next piece: c + 64 = c + 38 + 26
-        p += 26;
-        r += 1;
-        if (p >= kPieces) {
-            p -= kPieces;
-            r += 1;
-        }
-    }
-    // all lookups are issued before the first one is used
-#pragma unroll
-    for (int k = 0; k < kRowGathers; k++) asm volatile("" : "+v"(rows[k]));
-#pragma unroll
-    for (int k = 0; k < kScaleGathers; k++)
-        gather4(row_offset(row_of_lane, SMLA_SCALE_OFFSET + 4 * (2 * k + (lane >> 5))), rsrc,
-                slot_lds + kScaleTable + 256 * k);
-#pragma unroll
-    for (int k = 0; k < kRowGathers; k++) gather16(row_offset(rows[k], offs[k]), rsrc, slot_lds + 1024 * k);
+// Position of the list entries of a tile in an LDS slot: the unused group-7
+// row of its scale table.
+constexpr int kEntryTable = kScaleTable + 7 * kTile * 4;
+
+// List entries of one tile (token t = lane & 31 at byte 4t of the table, for
+// lanes 0..31) straight into LDS.  The buffer resource covers the chunk's
+// entries, so an entry past the chunk reads 0 (and is masked by its index).
+__device__ __forceinline__ void load_entries_lds(uint32_t first_entry, i32x4 idx_rsrc, uint32_t slot_lds,
+                                                 int lane) {
+    if (lane < 32) gather4(4u * (first_entry + lane), idx_rsrc, slot_lds + kEntryTable);
 }
 
 // One 32-token tile for one wave: 16 heads x the full latent.  st is the
@@ -296,7 +346,7 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
                                              float logit_factor) {
     const int qg = lane >> 4, ln = lane & 15;
 
-    // group scales, transposed: sT[g * 32 + t] = scale g of token t
+    // group scales, transposed: sT[g * 32 + s] = scale g of the row in LDS position s
     lds_cf32* sT = (lds_cf32*)(st + kScaleTable);
 
     // ---------------- S^T = K . Q^T per 16-token half; lane group q takes
@@ -306,11 +356,14 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
     u32x4 raw[2][7];
     u32x4 rr[2][2];
     auto load_half = [&](int tt) {
-        const lds_u8* krow = st + (16 * tt + ln) * kRowLds;
+        // pieces 4g + qg (codes) and rope pieces 2qg, 2qg + 1 of token 16tt + ln;
+        // piece 4g + qg sits 2048 g bytes after piece qg
+        const int pos = lds_pos(16 * tt + ln);
+        const lds_u8* kb = st + piece_addr(qg, pos);
 #pragma unroll
-        for (int g = 0; g < 7; g++) raw[tt][g] = *(lds_cu32x4*)(krow + 64 * g + 16 * qg);
-        rr[tt][0] = *(lds_cu32x4*)(krow + kLdsRope + 32 * qg);
-        rr[tt][1] = *(lds_cu32x4*)(krow + kLdsRope + 32 * qg + 16);
+        for (int g = 0; g < 7; g++) raw[tt][g] = *(lds_cu32x4*)(kb + 2048 * g);
+        rr[tt][0] = *(lds_cu32x4*)(st + piece_addr(kCodePieces + 2 * qg, pos));
+        rr[tt][1] = *(lds_cu32x4*)(st + piece_addr(kCodePieces + 2 * qg + 1, pos));
     };
     load_half(0);
     load_half(1);
@@ -332,7 +385,7 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
         f32x4 v = acc[7];
 #pragma unroll
         for (int g = 0; g < 7; g++)
-            v += *(lds_cf32x4*)(sT + g * kTile + 16 * tt + 4 * qg) * acc[g];
+            v += *(lds_cf32x4*)(sT + g * kTile + lds_pos(16 * tt + 4 * qg)) * acc[g];
         s[tt] = v;
     }
 #pragma unroll
@@ -373,18 +426,26 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
     // slot_token(8q + r), then slot_token(8q + 4 + r), columns 4c..4c+3 of each
     // 16-column block.  The reads of group g + 1 are issued before group g is
     // converted (one wave per SIMD has no other wave to hide LDS latency).
-    const lds_u8* tr_row = st + slot_token(8 * qg + (ln >> 1)) * kRowLds + 8 * (ln & 1);
-    const int col = 8 * (ln & 3);
-    const lds_u8* r0 = st + slot_token(8 * qg + (ln >> 2)) * kRowLds + kLdsRope + col;
-    const lds_u8* r1 = st + slot_token(8 * qg + 4 + (ln >> 2)) * kRowLds + kLdsRope + col;
+    // value pieces 4g + cb of this lane's token: piece cb plus 2048 g bytes
+    const int vpos = lds_pos(slot_token(8 * qg + (ln >> 1)));
+    const lds_u8* tr_cb[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) tr_cb[cb] = st + piece_addr(cb, vpos, ln & 1);
+    // rope bytes 32 dt + 8 (ln & 3): piece 28 + 2 dt + ((ln & 3) >> 1), half
+    // ln & 1; dt and dt + 2 are 2048 bytes apart
+    const int rpos0 = lds_pos(slot_token(8 * qg + (ln >> 2)));
+    const int rpos1 = lds_pos(slot_token(8 * qg + 4 + (ln >> 2)));
+    const int rp = kCodePieces + ((ln & 3) >> 1);
+    const lds_u8* r0[2] = {st + piece_addr(rp, rpos0, ln & 1), st + piece_addr(rp + 2, rpos0, ln & 1)};
+    const lds_u8* r1[2] = {st + piece_addr(rp, rpos1, ln & 1), st + piece_addr(rp + 2, rpos1, ln & 1)};
     i32x2 vraw[2][4];
     f32x4 svv[2][2];
     auto load_group = [&](int g, int buf) {
 #pragma unroll
         for (int cb = 0; cb < 4; cb++)
-            vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_row + 64 * g + 16 * cb));
-        svv[buf][0] = *(lds_cf32x4*)(sT + g * kTile + 4 * qg);
-        svv[buf][1] = *(lds_cf32x4*)(sT + g * kTile + 16 + 4 * qg);
+            vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_cb[cb] + 2048 * g));
+        svv[buf][0] = *(lds_cf32x4*)(sT + g * kTile + lds_pos(4 * qg));
+        svv[buf][1] = *(lds_cf32x4*)(sT + g * kTile + lds_pos(16 + 4 * qg));
     };
     load_group(0, 0);
     s16x4 rv[4][2];
@@ -395,8 +456,8 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
         if (g == 1) {
 #pragma unroll
             for (int dt = 0; dt < 4; dt++) {
-                rv[dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 32 * dt));
-                rv[dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1 + 32 * dt));
+                rv[dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0[dt & 1] + 2048 * (dt >> 1)));
+                rv[dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r1[dt & 1] + 2048 * (dt >> 1)));
             }
         }
         // weights fp16(p * scale_g); exact fp8 -> fp16 value codes
@@ -489,11 +550,17 @@ __device__ __forceinline__ void combine_row(const float* o_part, const float* ls
     if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
-// The combine as its own kernel: one wave per (b, h).
+// The combine as its own kernel: one wave per (b, h), four rows per
+// workgroup.  When the grid is a multiple of 8, workgroup ids are remapped like
+// the decode kernel's, so that XCD x merges the rows of the same contiguous
+// range of sequences whose partials its L2 received from the decode kernel
+// (exactly so when the batch is a multiple of 8).
 __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, const float* lse_part,
                                                            int32_t rows, int32_t nsplit,
                                                            uint16_t* out, float* lse) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    int bid = blockIdx.x;
+    if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+    const int row = bid * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     combine_row(o_part, lse_part, row, nsplit, out, lse, threadIdx.x & 63);
 }
@@ -550,35 +617,52 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     float m_run = -INFINITY;   // base of the exponentials for this lane's head (log2 units)
     float l_run = 0.f;         // partial sum of weights over this lane's tokens
 
-    // ---- tiles wave, wave + 4, ...  The list entries of tile i + 2 are loaded
-    // while tile i is computed and checked only after the next wait for the
-    // gathers (a check right after the load would make that wait cover the
-    // gathers just issued and stall on them).
+    // ---- tiles wave, wave + 4, ...  The gather of tile i + 1 is issued when
+    // tile i has landed and overlaps its compute.  (Gathering the first two
+    // tiles together measured no faster: the first one then lands later.)
+    // The first three tiles' list entries are loaded with the query before any
+    // gather; the entries of tile i + 2 go straight into LDS with the gathers
+    // of tile i + 1 and are read after the next wait.  An entry loaded into
+    // registers while gathers are in flight would make the compiler's own wait
+    // for it cover those gathers.
     const int my_n = wave < ntiles ? (ntiles - 1 - wave) / kWaves + 1 : 0;
     lds_u8* my_lds = lds + wave * kWaveLds;
     const uint32_t my_lds_addr = (uint32_t)(uintptr_t)my_lds;
-    auto entry = [&](int i) { return (wave + kWaves * i) * kTile + (lane & 31); };
-    // list entry of token (lane & 31) of tile i < my_n (clamped into the chunk)
-    auto load_entry = [&](int i) -> int { return idx_b[min(entry(i), n_ent - 1)]; };
+    const i32x4 idx_rsrc = row_rsrc((const uint8_t*)idx_b, 4u * (uint32_t)n_ent);
+    auto first_entry = [&](int i) { return (wave + kWaves * i) * kTile; };
+    // list entry of token (lane & 31) of tile i < my_n
+    auto load_entry = [&](int i) -> int { return idx_b[min(first_entry(i) + (lane & 31), n_ent - 1)]; };
     // the row it selects, or -1 for a masked entry (past the list, negative,
     // or not below the sequence length)
-    auto sanitise = [&](int i, int v) -> int { return entry(i) < n_ent && v >= 0 && v < seqlen ? v : -1; };
-    int row_cur = -1, ent_next = -1;
-    if (my_n > 0) {
-        const int ent0 = load_entry(0);
-        ent_next = load_entry(min(1, my_n - 1));
-        row_cur = sanitise(0, ent0);
-        issue_tile_own(row_cur, rsrc, my_lds_addr, lane);
-    }
+    auto sanitise = [&](int i, int v) -> int {
+        return first_entry(i) + (lane & 31) < n_ent && v >= 0 && v < seqlen ? v : -1;
+    };
+    int row_cur = -1, row_1 = -1, row_2 = -1;
     load_query();
+    if (my_n > 0) {
+        const int e0 = load_entry(0);
+        const int e1 = load_entry(min(1, my_n - 1));
+        const int e2 = load_entry(min(2, my_n - 1));
+        row_cur = sanitise(0, e0);
+        row_1 = sanitise(1, e1);
+        row_2 = sanitise(2, e2);
+        issue_tile(row_cur, rsrc, my_lds_addr, lane);
+    }
     pin_state(qop, acc_o);
     for (int i = 0; i < my_n; i++) {
         pin_state(qop, acc_o);
-        wait_vmcnt<0>();   // tile i is in its slot; the entries of tile i + 1 are in registers
-        const int row_next = sanitise(i + 1, ent_next);
-        if (i + 1 < my_n) issue_tile_own(row_next, rsrc, my_lds_addr + ((i + 1) & 1) * kSlot, lane);
-        ent_next = load_entry(min(i + 2, my_n - 1));
-        const uint64_t vmask = __ballot(lane < kTile && row_cur >= 0);
+        wait_vmcnt<0>();   // tile i has landed, and the entries of tile i + 1 (i >= 2)
+        const int slot1 = (i + 1) & 1;
+        const int row_next = i == 0   ? row_1
+                             : i == 1 ? row_2
+                                      : sanitise(i + 1, ((lds_ci32*)(my_lds + slot1 * kSlot + kEntryTable))[lane & 31]);
+        if (i + 1 < my_n) {
+            issue_tile(row_next, rsrc, my_lds_addr + slot1 * kSlot, lane);
+            // into the slot being computed: its entry table is not read by the compute
+            if (i >= 1 && i + 2 < my_n)
+                load_entries_lds(first_entry(i + 2), idx_rsrc, my_lds_addr + (i & 1) * kSlot, lane);
+        }
+        const uint64_t vmask = mask_by_token(__ballot(lane < kTile && row_cur >= 0));
         compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor);
         row_cur = row_next;
     }
