@@ -407,6 +407,10 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
         // the first kept tokens only set the base: the accumulators are still zero
         if (__any(m_run != -INFINITY)) {
             l_run *= alpha;
+            // the accumulator lives in AGPRs; this keeps its copy to VGPRs (for
+            // the multiply) inside this rarely taken branch
+#pragma unroll
+            for (int i = 0; i < 32; i++) asm volatile("" : "+a"(acc_o[i]));
 #pragma unroll
             for (int i = 0; i < 32; i++) acc_o[i] *= alpha;
         }
