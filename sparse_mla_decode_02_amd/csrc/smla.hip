@@ -624,8 +624,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     // ---- tiles wave, wave + 4, ...  The gather of tile i + 1 is issued when
     // tile i has landed and overlaps its compute.  (Gathering the first two
     // tiles together measured no faster: the first one then lands later.)
-    // The first three tiles' list entries are loaded with the query before any
-    // gather; the entries of tile i + 2 go straight into LDS with the gathers
+    // The first three tiles' list entries are loaded before any gather (the
+    // query after the first gather); the entries of tile i + 2 go straight into LDS with the gathers
     // of tile i + 1 and are read after the next wait.  An entry loaded into
     // registers while gathers are in flight would make the compiler's own wait
     // for it cover those gathers.
@@ -642,7 +642,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         return first_entry(i) + (lane & 31) < n_ent && v >= 0 && v < seqlen ? v : -1;
     };
     int row_cur = -1, row_1 = -1, row_2 = -1;
-    load_query();
     if (my_n > 0) {
         const int e0 = load_entry(0);
         const int e1 = load_entry(min(1, my_n - 1));
@@ -652,6 +651,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         row_2 = sanitise(2, e2);
         issue_tile(row_cur, rsrc, my_lds_addr, lane);
     }
+    // the query lands while the first tile is gathered
+    load_query();
     pin_state(qop, acc_o);
     for (int i = 0; i < my_n; i++) {
         pin_state(qop, acc_o);
@@ -685,25 +686,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
 #pragma unroll
     for (int w = 0; w < kWaves; w++) M = fmaxf(M, stat[w * 32 + ln]);
     const float Ms0 = M == -INFINITY ? 0.f : M;
+    // weight of wave w's accumulator for head ln: 2^(m_w - M)
+    float wgt[kWaves];
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) L += __builtin_amdgcn_exp2f(stat[w * 32 + ln] - Ms0) * stat[w * 32 + 16 + ln];
-    const float aw = __builtin_amdgcn_exp2f(m_run - Ms0);
+    for (int w = 0; w < kWaves; w++) {
+        wgt[w] = __builtin_amdgcn_exp2f(stat[w * 32 + ln] - Ms0);
+        L += wgt[w] * stat[w * 32 + 16 + ln];
+    }
+    // the accumulators go to LDS unscaled, straight from their AGPRs
     lds_f32x4* part = (lds_f32x4*)(lds + wave * kAccBytes);
 #pragma unroll
-    for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i] * aw;
+    for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i];
     __syncthreads();
 
     // wave w finishes accumulator blocks 8w..8w+7; block i holds columns
     // 16i + 4qg + j for head ln
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const float lse2 = L > 0.f ? M + log2f(L) : -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) wgt[w] *= inv;
     const int64_t bh = (int64_t)b * a.heads + head;
     const bool final_out = a.nsplit == 1 && !a.force_partials;
-    auto block_sum = [&](int i) -> f32x4 {
-        f32x4 v = ((lds_cf32x4*)lds)[i * 64 + lane];
+    auto block_sum = [&](int i) -> f32x4 {   // the normalised output block
+        f32x4 v = wgt[0] * ((lds_cf32x4*)lds)[i * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kWaves; w++) v += ((lds_cf32x4*)(lds + w * kAccBytes))[i * 64 + lane];
+        for (int w = 1; w < kWaves; w++) v += wgt[w] * ((lds_cf32x4*)(lds + w * kAccBytes))[i * 64 + lane];
         return v;
     };
     const int i0 = wave * (32 / kWaves);
@@ -713,14 +721,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         for (int ii = 0; ii < 32 / kWaves; ii++) {
             const f32x4 v = block_sum(i0 + ii);
             u32x2 w;
-            w[0] = pack_bf16x2(v[0] * inv, v[1] * inv);
-            w[1] = pack_bf16x2(v[2] * inv, v[3] * inv);
+            w[0] = pack_bf16x2(v[0], v[1]);
+            w[1] = pack_bf16x2(v[2], v[3]);
             *(u32x2*)(o + 16 * (i0 + ii)) = w;
         }
     } else {
         float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 4 * qg;
 #pragma unroll
-        for (int ii = 0; ii < 32 / kWaves; ii++) *(f32x4*)(o + 16 * (i0 + ii)) = block_sum(i0 + ii) * inv;
+        for (int ii = 0; ii < 32 / kWaves; ii++) *(f32x4*)(o + 16 * (i0 + ii)) = block_sum(i0 + ii);
     }
     if (wave == 0 && qg == 0) {
         if (final_out) a.lse[bh] = lse2 * kLn2;
