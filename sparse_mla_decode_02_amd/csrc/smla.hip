@@ -215,37 +215,34 @@ __device__ __forceinline__ uint32_t row_offset(int row, uint32_t off) {
     return (uint32_t)__mul24(row, kRowBytes) + off;
 }
 
-// 16-byte (4-byte) gather of one lane straight into LDS at lds_base + 16 *
-// lane (+ 4 * lane): buffer_load_dwordx4 / _dword with the lds bit; the LDS
-// base goes through M0 and must be wave-uniform.  Written as inline assembly
-// so that the compiler does not treat every later LDS read as dependent on
-// every gather in flight; the ordering is explicit instead (s_waitcnt vmcnt
-// before a slot is read, and a workgroup barrier where slots are shared).
-__device__ __forceinline__ void gather16(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory", "m0");
-}
-
+// 4-byte gather of one lane straight into LDS at lds_base + 4 * lane:
+// buffer_load_dword with the lds bit; the LDS base goes through M0 and must be
+// wave-uniform.  Written as inline assembly so that the compiler does not
+// treat every later LDS read as dependent on every gather in flight: the
+// ordering is explicit instead (wait_vmcnt before the destination is read).
+// No memory clobber, for the same reason as the gathers below.
 __device__ __forceinline__ void gather4(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory", "m0");
+                 : "m0");
 }
 
-// The same with a constant byte offset kOff (< 4096) in the instruction.  The
+// 16-byte (4-byte) gathers with a constant byte offset kOff (< 4096) in the
+// instruction; lane l writes lds_base + 16 l (+ 4 l).  The
 // instruction offset moves the LDS destination as well as the source (checked
 // on gfx950), so M0 is set kOff bytes lower to keep the destination at
-// lds_base (which is at least kOff).
+// lds_base (which is at least kOff).  These carry no memory clobber, so that
+// the compiler may schedule the compute's LDS reads of the other slot around
+// them: the gathers only write a slot that nothing reads until the next
+// wait_vmcnt, which is a compiler barrier.
 template <int kOff>
 __device__ __forceinline__ void gather16_at(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
     static_assert(kOff >= 0 && kOff < 4096, "buffer instruction offset");
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base - kOff)), "n"(kOff)
-                 : "memory", "m0");
+                 : "m0");
 }
 
 template <int kOff>
@@ -254,7 +251,7 @@ __device__ __forceinline__ void gather4_at(uint32_t voff, i32x4 rsrc, uint32_t l
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen offset:%3 lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base - kOff)), "n"(kOff)
-                 : "memory", "m0");
+                 : "m0");
 }
 
 template <int K, int N, typename F>
@@ -266,10 +263,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+// It is also a compiler barrier for memory accesses: LDS reads of a slot that
+// the gathers fill must not be moved above the wait for them.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
 }
 
 // Workgroup barrier without a memory fence: only this wave's LDS operations are
@@ -307,24 +307,47 @@ struct DecodeArgs {
 // offset registers.  Scale gather k loads scale 2k + (l >> 5) of position
 // l & 31 into row 2k + (l >> 5) of the table; the last one leaves out group 7
 // (padding), whose row holds list entries instead (see load_entries_lds).
-__device__ __forceinline__ void issue_tile(int row, i32x4 rsrc, uint32_t slot_lds, int lane) {
+struct TileGather {
+    uint32_t v0, v1;     // source offsets for the blocks of positions 0..15 and 16..31
+    uint32_t vscale;     // source offset of this lane's scale pair
+    uint32_t slot;       // LDS slot address
+};
+
+__device__ __forceinline__ TileGather plan_tile(int row, uint32_t slot_lds, int lane) {
     const int row0 = __builtin_amdgcn_ds_bpermute(4 * (lane >> 2), row);
     const int row1 = __builtin_amdgcn_ds_bpermute(4 * (16 + (lane >> 2)), row);
     const uint32_t pp = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    const uint32_t vscale = row_offset(row, SMLA_SCALE_OFFSET + 4u * ((uint32_t)lane >> 5));
+    TileGather g;
+    g.v0 = row_offset(row0, 16u * pp);
+    g.v1 = row_offset(row1, 16u * pp);
+    g.vscale = row_offset(row, SMLA_SCALE_OFFSET + 4u * ((uint32_t)lane >> 5));
+    g.slot = slot_lds;
+    return g;
+}
+
+__device__ __forceinline__ void issue_scales(const TileGather& g, i32x4 rsrc, int lane) {
     static_for<0, kScaleGathers - 1>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        gather4_at<8 * k>(vscale, rsrc, slot_lds + kScaleTable + 256 * k);
+        gather4_at<8 * k>(g.vscale, rsrc, g.slot + kScaleTable + 256 * k);
     });
-    if (lane < 32) gather4_at<8 * (kScaleGathers - 1)>(vscale, rsrc, slot_lds + kScaleTable + 256 * (kScaleGathers - 1));
-    const uint32_t v0 = row_offset(row0, 16u * pp);
-    const uint32_t v1 = row_offset(row1, 16u * pp);
-    static_for<0, kRowGathers / 2>([&](auto jc) {
+    if (lane < 32) gather4_at<8 * (kScaleGathers - 1)>(g.vscale, rsrc, g.slot + kScaleTable + 256 * (kScaleGathers - 1));
+}
+
+// Blocks 2j and 2j + 1 for j in [J0, J1).
+template <int J0, int J1>
+__device__ __forceinline__ void issue_blocks(const TileGather& g, i32x4 rsrc) {
+    static_for<J0, J1>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int off = 64 * j + (4 * j >= kCodePieces ? 32 : 0);
-        gather16_at<off>(v0, rsrc, slot_lds + 1024 * (2 * j));
-        gather16_at<off>(v1, rsrc, slot_lds + 1024 * (2 * j + 1));
+        gather16_at<off>(g.v0, rsrc, g.slot + 1024 * (2 * j));
+        gather16_at<off>(g.v1, rsrc, g.slot + 1024 * (2 * j + 1));
     });
+}
+
+__device__ __forceinline__ void issue_tile(int row, i32x4 rsrc, uint32_t slot_lds, int lane) {
+    const TileGather g = plan_tile(row, slot_lds, lane);
+    issue_scales(g, rsrc, lane);
+    issue_blocks<0, kRowGathers / 2>(g, rsrc);
 }
 
 // Position of the list entries of a tile in an LDS slot: the unused group-7
@@ -341,9 +364,13 @@ __device__ __forceinline__ void load_entries_lds(uint32_t first_entry, i32x4 idx
 
 // One 32-token tile for one wave: 16 heads x the full latent.  st is the
 // tile's LDS slot; vmask marks the kept tokens.
+// issue_part(stage) is called at four points (stages 0..3) to spread the next
+// tile's gathers over the compute: a run of gather instructions stalls the
+// wave while the address unit drains them.
+template <typename IssuePart>
 __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, const bf16x8 (&qop)[16],
                                              f32x4 (&acc_o)[32], float& m_run, float& l_run, int lane,
-                                             float logit_factor) {
+                                             float logit_factor, IssuePart&& issue_part) {
     const int qg = lane >> 4, ln = lane & 15;
 
     // group scales, transposed: sT[g * 32 + s] = scale g of the row in LDS position s
@@ -367,6 +394,7 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
     };
     load_half(0);
     load_half(1);
+    issue_part(std::integral_constant<int, 0>{});
     f32x4 s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
@@ -396,6 +424,8 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
             s[tt][j] = ((vmask >> (16 * tt + 4 * qg + j)) & 1) ? z : -INFINITY;
         }
 
+    issue_part(std::integral_constant<int, 1>{});
+
     // ---------------- online softmax (log2 domain), lazy rescale
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -423,6 +453,8 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
         p[j] = __builtin_amdgcn_exp2f(s[j >> 2][j & 3] - base);
         l_run += p[j];
     }
+
+    issue_part(std::integral_constant<int, 2>{});
 
     // ---------------- O^T += V^T . P^T
     // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2),
@@ -476,6 +508,7 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
             acc_o[4 * g + cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 codes_to_f16((uint32_t)vraw[cur][cb][0], (uint32_t)vraw[cur][cb][1]), bop, acc_o[4 * g + cb],
                 0, 0, 0);
+        if (g == 3) issue_part(std::integral_constant<int, 3>{});
     }
     {
         // rope: bf16 values as stored; weights split into bf16 high and low parts
@@ -661,14 +694,30 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         const int row_next = i == 0   ? row_1
                              : i == 1 ? row_2
                                       : sanitise(i + 1, ((lds_ci32*)(my_lds + slot1 * kSlot + kEntryTable))[lane & 31]);
-        if (i + 1 < my_n) {
-            issue_tile(row_next, rsrc, my_lds_addr + slot1 * kSlot, lane);
-            // into the slot being computed: its entry table is not read by the compute
-            if (i >= 1 && i + 2 < my_n)
-                load_entries_lds(first_entry(i + 2), idx_rsrc, my_lds_addr + (i & 1) * kSlot, lane);
+        // the gathers of tile i + 1: the scales and two blocks now, the rest
+        // within the logit product of tile i (early enough for the memory-bound
+        // lists); then the entries of tile i + 2, into the slot being computed
+        // (its entry table is not read by the compute)
+        const bool more = i + 1 < my_n;
+        TileGather tg = {};
+        if (more) {
+            tg = plan_tile(row_next, my_lds_addr + slot1 * kSlot, lane);
+            issue_scales(tg, rsrc, lane);
+            issue_blocks<0, 2>(tg, rsrc);
         }
+        auto issue_part = [&](auto stage) {
+            if (!more) return;
+            constexpr int k = decltype(stage)::value;
+            if constexpr (k == 0) {
+                issue_blocks<2, 6>(tg, rsrc);
+            } else if constexpr (k == 1) {
+                issue_blocks<6, kRowGathers / 2>(tg, rsrc);
+                if (i >= 1 && i + 2 < my_n)
+                    load_entries_lds(first_entry(i + 2), idx_rsrc, my_lds_addr + (i & 1) * kSlot, lane);
+            }
+        };
         const uint64_t vmask = mask_by_token(__ballot(lane < kTile && row_cur >= 0));
-        compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor);
+        compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor, issue_part);
         row_cur = row_next;
     }
     wait_vmcnt<0>();
