@@ -541,41 +541,45 @@ __device__ __forceinline__ void pin_state(bf16x8 (&qop)[16], f32x4 (&acc_o)[32])
 }
 
 // Log-sum-exp merge of the split partials of one (b, h) row by one wave, 8
-// columns per lane.  The partial outputs are read four splits at a time with
-// all loads issued before they are used.  An empty split (lse = -inf) has
-// weight exp(-inf) = 0 and a zero partial.
+// columns per lane.  Splits are taken four at a time: the four log-sum-exps
+// (scalar loads) and partial outputs (vector loads) of a group are all issued
+// before any is used, so a row with at most four splits costs one round trip
+// to memory; later groups are folded in with a running-maximum rescale.  Split
+// indices past the end are clamped and given weight 0.  An empty split (lse =
+// -inf) has weight exp(-inf) = 0 and a zero partial.
 __device__ __forceinline__ void combine_row(const float* o_part, const float* lse_part, int64_t row,
                                             int nsplit, uint16_t* out, float* lse, int lane) {
     const float* lp = lse_part + row * nsplit;
-    float M = -INFINITY;
-    for (int i = 0; i < nsplit; i++) M = fmaxf(M, lp[i]);
-    const float Ms = M == -INFINITY ? 0.f : M;
     const float* src = o_part + row * nsplit * kLatent + 8 * lane;
+    float M = -INFINITY, W = 0.f;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    float W = 0.f;
-    int i = 0;
-    for (; i + 4 <= nsplit; i += 4) {
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+        float l[4];
         f32x4 lo[4], hi[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            lo[k] = *(const f32x4*)(src + (i + k) * kLatent);
-            hi[k] = *(const f32x4*)(src + (i + k) * kLatent + 4);
+            const int sk = min(s0 + k, nsplit - 1);
+            l[k] = lp[sk];
+            lo[k] = *(const f32x4*)(src + sk * kLatent);
+            hi[k] = *(const f32x4*)(src + sk * kLatent + 4);
         }
+        float m = M;
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            if (s0 + k < nsplit) m = fmaxf(m, l[k]);
+        const float ms = m == -INFINITY ? 0.f : m;
+        const float f = __expf(M - ms);   // 0 while nothing was folded in
+        W *= f;
+        acc0 *= f;
+        acc1 *= f;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            const float w = __expf(lp[i + k] - Ms);
+            const float w = s0 + k < nsplit ? __expf(l[k] - ms) : 0.f;
             W += w;
             acc0 += w * lo[k];
             acc1 += w * hi[k];
         }
-    }
-    for (; i < nsplit; i++) {
-        const f32x4 lo = *(const f32x4*)(src + i * kLatent);
-        const f32x4 hi = *(const f32x4*)(src + i * kLatent + 4);
-        const float w = __expf(lp[i] - Ms);
-        W += w;
-        acc0 += w * lo;
-        acc1 += w * hi;
+        M = m;
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     u32x4 pk;
