@@ -46,8 +46,14 @@ def lib():
         L.oracle_bf16_value.restype = f64
         L.oracle_dequant_row.argtypes = [vp, vp]
         L.oracle_dequant_row.restype = None
+        L.oracle_dequant_row_fmt.argtypes = [vp, i32, vp]
+        L.oracle_dequant_row_fmt.restype = None
+        L.oracle_ue8m0_value.argtypes = [ctypes.c_uint8]
+        L.oracle_ue8m0_value.restype = f64
         L.oracle_decode.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, f64, vp, vp, i32]
         L.oracle_decode.restype = i32
+        L.oracle_decode_fmt.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, f64, vp, vp, i32, i32]
+        L.oracle_decode_fmt.restype = i32
         L.oracle_decode_padded512.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, f64, vp, vp]
         L.oracle_decode_padded512.restype = i32
         _lib = L
@@ -62,20 +68,29 @@ def e4m3fn_value(code: int) -> float:
     return lib().oracle_e4m3fn_value(int(code))
 
 
-def dequant_row(row: np.ndarray) -> np.ndarray:
+ROW_BYTES_OF_FORMAT = {0: 640, 1: 584}
+
+
+def ue8m0_value(e: int) -> float:
+    return lib().oracle_ue8m0_value(int(e))
+
+
+def dequant_row(row: np.ndarray, row_format: int = 0) -> np.ndarray:
     row = np.ascontiguousarray(row, dtype=np.uint8)
-    assert row.shape == (640,)
+    assert row.shape == (ROW_BYTES_OF_FORMAT[row_format],)
     K = np.empty(512, dtype=np.float64)
-    lib().oracle_dequant_row(_p(row), _p(K))
+    lib().oracle_dequant_row_fmt(_p(row), int(row_format), _p(K))
     return K
 
 
 def decode_raw(q_bits, cache, kv_seq_stride, idx, seqlens, heads, scale, *, padded512=False,
-               nthreads=0, idx_cols=None, idx_offset=0, idx_row_stride=None):
+               nthreads=0, idx_cols=None, idx_offset=0, idx_row_stride=None, row_format=0):
     """out fp64 [B,H,512], lse fp64 [B,H], threads used.
 
     ``idx`` int32 [B, topk]; the list of sequence b is
     idx[b, idx_offset : idx_offset + idx_cols] (a split of the list).
+    ``row_format`` 0: 640-byte rows with fp32 scales; 1: 584-byte rows with
+    UE8M0 scales.
     """
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
@@ -87,17 +102,19 @@ def decode_raw(q_bits, cache, kv_seq_stride, idx, seqlens, heads, scale, *, padd
     out = np.zeros((B, heads, 512), dtype=np.float64)
     lse = np.zeros((B, heads), dtype=np.float64)
     assert cache.dtype == np.uint8 and cache.flags.c_contiguous
-    assert cache.size >= B * kv_seq_stride * 640
+    assert cache.size >= B * kv_seq_stride * ROW_BYTES_OF_FORMAT[row_format]
     idx_view = idx[:, idx_offset:]
     ptr = ctypes.c_void_p(idx.ctypes.data + 4 * idx_offset)
     stride = topk if idx_row_stride is None else idx_row_stride
     if padded512:
+        assert row_format == 0
         used = lib().oracle_decode_padded512(_p(q_bits), _p(cache), kv_seq_stride, ptr, stride,
                                              _p(seqlens), B, heads, idx_cols, float(scale),
                                              _p(out), _p(lse))
     else:
-        used = lib().oracle_decode(_p(q_bits), _p(cache), kv_seq_stride, ptr, stride, _p(seqlens),
-                                   B, heads, idx_cols, float(scale), _p(out), _p(lse), int(nthreads))
+        used = lib().oracle_decode_fmt(_p(q_bits), _p(cache), kv_seq_stride, ptr, stride, _p(seqlens),
+                                       B, heads, idx_cols, float(scale), _p(out), _p(lse), int(nthreads),
+                                       int(row_format))
     del idx_view
     return out, lse, used
 
@@ -108,7 +125,7 @@ def decode(w, cache=None, **kw):
         from workloads import build_host_cache
         cache = build_host_cache(w)
     out, lse, _ = decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads,
-                             w.scale, **kw)
+                             w.scale, row_format=w.row_format, **kw)
     return out, lse
 
 
@@ -128,7 +145,7 @@ def decode_splits(w, nsplit, cache=None, chunk=None):
     l = np.zeros((w.batch, w.heads, nsplit))
     for i, (lo, hi) in enumerate(split_bounds(w.topk, nsplit, chunk)):
         oi, li, _ = decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads,
-                               w.scale, idx_offset=lo, idx_cols=hi - lo)
+                               w.scale, idx_offset=lo, idx_cols=hi - lo, row_format=w.row_format)
         o[:, :, i] = oi
         l[:, :, i] = li
     return o, l

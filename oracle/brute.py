@@ -15,15 +15,22 @@ import torch
 from scipy.special import logsumexp
 
 
-def dequant_rows_torch(rows: np.ndarray) -> np.ndarray:
-    """rows uint8 [N,640] -> K fp64 [N,512] using torch's dtype conversions."""
+def dequant_rows_torch(rows: np.ndarray, row_format: int = 0) -> np.ndarray:
+    """rows uint8 [N,640] (format 0) or [N,584] (format 1, UE8M0 scales) ->
+    K fp64 [N,512] using torch's dtype conversions; a UE8M0 byte e is the
+    power of two 2^(e - 127) (torch.exp2 in fp64), 255 NaN."""
     rows = np.ascontiguousarray(rows, dtype=np.uint8)
     n = rows.shape[0]
     t = torch.from_numpy(rows)
     codes = t[:, :448].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
-    scales = t[:, 448:476].contiguous().view(torch.float32).to(torch.float64)  # [N,7]
+    if row_format == 1:
+        e = t[:, 448:455].to(torch.float64)                                     # [N,7]
+        scales = torch.where(e == 255, torch.full_like(e, float("nan")), torch.exp2(e - 127))
+        rope = t[:, 456:584].contiguous().view(torch.bfloat16).to(torch.float64)
+    else:
+        scales = t[:, 448:476].contiguous().view(torch.float32).to(torch.float64)  # [N,7]
+        rope = t[:, 480:608].contiguous().view(torch.bfloat16).to(torch.float64)
     nope = codes * scales.repeat_interleave(64, dim=1)
-    rope = t[:, 480:608].contiguous().view(torch.bfloat16).to(torch.float64)
     return torch.cat([nope, rope], dim=1).numpy().reshape(n, 512)
 
 
@@ -32,18 +39,18 @@ def q_values(q_bits: np.ndarray) -> np.ndarray:
         .view(torch.bfloat16).to(torch.float64).numpy()
 
 
-def brute_decode(q_bits, cache, kv_seq_stride, idx, seqlens, scale):
+def brute_decode(q_bits, cache, kv_seq_stride, idx, seqlens, scale, row_format=0):
     """Dense fp64 attention restricted to the selected rows (tiny inputs)."""
     q = q_values(q_bits)                       # [B,H,512]
     B, H, _ = q.shape
-    cache = cache.reshape(B, kv_seq_stride, 640)
+    cache = cache.reshape(B, kv_seq_stride, 584 if row_format == 1 else 640)
     out = np.zeros((B, H, 512))
     lse = np.full((B, H), -np.inf)
     for b in range(B):
         sel = [int(t) for t in idx[b] if 0 <= t < seqlens[b]]
         if not sel:
             continue
-        K = dequant_rows_torch(cache[b, sel])  # [n,512]
+        K = dequant_rows_torch(cache[b, sel], row_format)  # [n,512]
         z = scale * (q[b] @ K.T)               # [H,n]
         l = logsumexp(z, axis=1)
         p = np.exp(z - l[:, None])

@@ -23,9 +23,15 @@
  * With no selected entry the result is out = 0, lse = -inf.  It re-dequantises
  * every row for every head (the naive per-head loop), parallel over (b, h).
  *
- * Cache layout (its own constants, read from the row format description):
- * row stride 640 bytes; nope codes at 0..447; fp32 scales at 448 (7 used,
- * the 8th slot is padding); bf16 rope at 480..607.
+ * Cache layouts (its own constants, read from the row format descriptions):
+ *   format 0: row stride 640 bytes; nope codes at 0..447; fp32 scales at 448
+ *             (7 used, the 8th slot is padding); bf16 rope at 480..607.
+ *   format 1: row stride 584 bytes; nope codes at 0..447; UE8M0 scales at
+ *             448 (one byte per group, 7 used, the 8th is padding); bf16 rope
+ *             at 456..583.  The pages give the deployed model's scales as
+ *             unsigned 8-bit exponent-only values, one per 64-column group
+ *             ("The Power-of-Two Trap", section "Input Knowledge Required");
+ *             the value of byte e is read as 2^(e - 127), with e = 255 NaN.
  */
 #include <math.h>
 #include <stdint.h>
@@ -41,6 +47,9 @@
 #define OR_GROUP 64
 #define OR_SCALE_AT 448
 #define OR_ROPE_AT 480
+#define OR_UE8M0_ROW_STRIDE 584
+#define OR_UE8M0_SCALE_AT 448
+#define OR_UE8M0_ROPE_AT 456
 
 /* OCP fp8 e4m3fn: sign, 4 exponent bits with bias 7, 3 mantissa bits.
  * Exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinities. */
@@ -71,16 +80,31 @@ static double f32_at(const uint8_t* p) {
     return (double)f;
 }
 
-/* Dequantise one cache row into K[512] (fp64, exact). */
-void oracle_dequant_row(const uint8_t* row, double* K) {
-    for (int i = 0; i < OR_NOPE; i++)
-        K[i] = oracle_e4m3fn_value(row[i]) * f32_at(row + OR_SCALE_AT + 4 * (i / OR_GROUP));
+/* UE8M0 scale byte: 2^(e - 127); 255 is NaN. */
+double oracle_ue8m0_value(uint8_t e) {
+    if (e == 0xFF) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+int oracle_row_stride(int fmt) { return fmt == 1 ? OR_UE8M0_ROW_STRIDE : OR_ROW_STRIDE; }
+
+/* Dequantise one cache row of format fmt into K[512] (fp64, exact). */
+void oracle_dequant_row_fmt(const uint8_t* row, int fmt, double* K) {
+    for (int i = 0; i < OR_NOPE; i++) {
+        const int g = i / OR_GROUP;
+        const double s = fmt == 1 ? oracle_ue8m0_value(row[OR_UE8M0_SCALE_AT + g])
+                                  : f32_at(row + OR_SCALE_AT + 4 * g);
+        K[i] = oracle_e4m3fn_value(row[i]) * s;
+    }
+    const int rope_at = fmt == 1 ? OR_UE8M0_ROPE_AT : OR_ROPE_AT;
     for (int k = 0; k < OR_ROPE; k++) {
         uint16_t b;
-        memcpy(&b, row + OR_ROPE_AT + 2 * k, 2);
+        memcpy(&b, row + rope_at + 2 * k, 2);
         K[OR_NOPE + k] = oracle_bf16_value(b);
     }
 }
+
+void oracle_dequant_row(const uint8_t* row, double* K) { oracle_dequant_row_fmt(row, 0, K); }
 
 /*
  * q:        bf16 bits [B][H][512]
@@ -90,10 +114,11 @@ void oracle_dequant_row(const uint8_t* row, double* K) {
  * out:      fp64 [B][H][512];  lse: fp64 [B][H]
  * nthreads: OpenMP threads (<= 0: library default).  Returns the thread count used.
  */
-int oracle_decode(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
-                  const int32_t* idx, int64_t idx_row_stride, const int32_t* seqlens,
-                  int B, int H, int topk, double scale, double* out, double* lse,
-                  int nthreads) {
+int oracle_decode_fmt(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
+                      const int32_t* idx, int64_t idx_row_stride, const int32_t* seqlens,
+                      int B, int H, int topk, double scale, double* out, double* lse,
+                      int nthreads, int fmt) {
+    const int64_t row_stride = oracle_row_stride(fmt);
     int used = 1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -117,7 +142,7 @@ int oracle_decode(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
         for (int j = 0; j < topk; j++) {
             int32_t t = idx[(int64_t)b * idx_row_stride + j];
             if (t < 0 || t >= seqlens[b]) continue;
-            oracle_dequant_row(kv + ((int64_t)b * kv_seq_stride + t) * OR_ROW_STRIDE, K);
+            oracle_dequant_row_fmt(kv + ((int64_t)b * kv_seq_stride + t) * row_stride, fmt, K);
             double z = 0.0;
             for (int d = 0; d < OR_LATENT; d++) z += qd[d] * K[d];
             z *= scale;
@@ -135,7 +160,7 @@ int oracle_decode(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
         for (int j = 0; j < topk; j++) {
             int32_t t = idx[(int64_t)b * idx_row_stride + j];
             if (t < 0 || t >= seqlens[b]) continue;
-            oracle_dequant_row(kv + ((int64_t)b * kv_seq_stride + t) * OR_ROW_STRIDE, K);
+            oracle_dequant_row_fmt(kv + ((int64_t)b * kv_seq_stride + t) * row_stride, fmt, K);
             double z = 0.0;
             for (int d = 0; d < OR_LATENT; d++) z += qd[d] * K[d];
             z *= scale;
@@ -147,6 +172,14 @@ int oracle_decode(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
         lse[bh] = M + log(L);
     }
     return used;
+}
+
+int oracle_decode(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
+                  const int32_t* idx, int64_t idx_row_stride, const int32_t* seqlens,
+                  int B, int H, int topk, double scale, double* out, double* lse,
+                  int nthreads) {
+    return oracle_decode_fmt(q, kv, kv_seq_stride, idx, idx_row_stride, seqlens, B, H, topk, scale, out,
+                             lse, nthreads, 0);
 }
 
 /*

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from oracle.brute import brute_decode, dequant_rows_torch, q_values
-from workloads import build_host_cache, config_workload, make_workload
+from workloads import build_host_cache, config_workload, make_workload, quantise_rows, ue8m0_exponents
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -192,3 +192,102 @@ def test_golden_regression():
     assert np.allclose(lse.ravel(), np.array(g["lse"]), rtol=0, atol=1e-12)
     sample = out.reshape(-1)[np.array(g["out_index"])]
     assert np.allclose(sample, np.array(g["out_value"]), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Row format 1: UE8M0 exponent-byte scales, 584-byte rows
+# ---------------------------------------------------------------------------
+
+def run_fmt(w):
+    cache = build_host_cache(w)
+    out, lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads,
+                                    w.scale, row_format=w.row_format)
+    return out, lse, cache
+
+
+def test_ue8m0_value_landmarks():
+    # byte e stands for 2^(e-127); 255 is the NaN encoding
+    assert oracle.ue8m0_value(127) == 1.0
+    assert oracle.ue8m0_value(128) == 2.0
+    assert oracle.ue8m0_value(126) == 0.5
+    assert oracle.ue8m0_value(0) == 2.0 ** -127
+    assert oracle.ue8m0_value(254) == 2.0 ** 127
+    assert np.isnan(oracle.ue8m0_value(255))
+
+
+@pytest.mark.parametrize("cfg", TINY)
+def test_ue8m0_oracle_matches_brute_force(cfg):
+    w = make_workload(row_format=1, **cfg)
+    out, lse, cache = run_fmt(w)
+    assert cache.shape[-1] == 584
+    bout, blse = brute_decode(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.scale,
+                              row_format=1)
+    scale = max(1.0, np.abs(bout).max())
+    assert np.abs(out - bout).max() <= 1e-12 * scale
+    fin = np.isfinite(blse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.abs(lse[fin] - blse[fin]).max() <= 1e-12 * max(1.0, np.abs(blse[fin]).max())
+
+
+def _reencode_fp32_scales(rows584: np.ndarray) -> np.ndarray:
+    """The same rows in the 640-byte layout, each exponent byte e written as the
+    fp32 number 2^(e-127) (exact for e in 1..254)."""
+    n = rows584.shape[0]
+    e = rows584[:, 448:455].astype(np.int32)
+    assert e.min() >= 1 and e.max() <= 254
+    s = np.ldexp(np.ones_like(e, dtype=np.float32), e - 127).astype(np.float32)
+    r = np.full((n, 640), 0xFF, dtype=np.uint8)
+    r[:, :448] = rows584[:, :448]
+    r[:, 448:476] = s.view(np.uint8).reshape(n, 28)
+    r[:, 480:608] = rows584[:, 456:584]
+    return r
+
+
+@pytest.mark.parametrize("cfg", TINY + [dict(seed=22, batch=2, heads=16, topk=64, seqlen=256,
+                                             q_mult=4.0)])
+def test_ue8m0_equals_fp32_scale_rows_bitwise(cfg):
+    # a UE8M0 row and the same row carrying its scale as an fp32 power of two
+    # describe the same numbers: results are identical bits
+    w = make_workload(row_format=1, **cfg)
+    out, lse, cache = run_fmt(w)
+    B, S, _ = cache.shape
+    full = np.full((B * S, 640), 0xFF, dtype=np.uint8)
+    flat = cache.reshape(B * S, 584)
+    used = np.unique(np.concatenate([b * S + w.idx[b][w.valid[b]] for b in range(B)]))
+    full[used] = _reencode_fp32_scales(flat[used])
+    out0, lse0, _ = oracle.decode_raw(w.q_bits, full.reshape(B, S, 640), w.kv_seq_stride, w.idx,
+                                      w.seqlens, w.heads, w.scale)
+    assert np.array_equal(out.view(np.uint64), out0.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), lse0.view(np.uint64))
+
+
+def test_ue8m0_quantiser_scales_are_tight_and_never_saturate():
+    rng = np.random.default_rng(7)
+    nope = (rng.standard_normal((64, 448)) * np.exp(rng.uniform(-20, 20, (64, 1)))).astype(np.float32)
+    nope[3, 64:128] = 0.0                                   # all-zero group -> e = 127
+    rows = quantise_rows(nope, np.zeros((64, 64), np.float32), row_format=1)
+    e = rows[:, 448:455].astype(np.int64)
+    amax = np.abs(nope.reshape(64, 7, 64)).max(axis=2).astype(np.float64)
+    s = np.ldexp(1.0, e - 127)
+    nz = amax > 0
+    assert np.all(amax[nz] / s[nz] <= 448.0)                # no code saturates
+    assert np.all(amax[nz] / (s[nz] / 2) > 448.0)           # the next smaller power would
+    assert e[3, 1] == 127
+    assert np.array_equal(ue8m0_exponents(np.array([448.0, 449.0, 224.0, 0.0])),
+                          np.array([127, 128, 126, 127], dtype=np.uint8))
+
+
+def test_ue8m0_pad_byte_is_never_read():
+    w = make_workload(seed=6, batch=2, heads=16, topk=32, seqlen=128, row_format=1)
+    out, lse, cache = run_fmt(w)
+    used = cache.reshape(-1, 584)[w.idx[0]]
+    assert np.all(used[:, 455] == 0xFF)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_ue8m0_dequant_row_matches_brute():
+    w = make_workload(seed=8, batch=1, heads=16, topk=16, seqlen=16, row_format=1)
+    rows = w.rows.reshape(-1, 584)
+    K = dequant_rows_torch(rows, row_format=1)
+    for i in range(rows.shape[0]):
+        assert np.array_equal(oracle.dequant_row(rows[i], row_format=1), K[i])

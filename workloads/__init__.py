@@ -13,6 +13,9 @@ from .generate import (  # noqa: F401
     NOPE,
     ROPE,
     ROW_BYTES,
+    ROW_BYTES_OF_FORMAT,
+    ROW_FMT_FP32,
+    ROW_FMT_UE8M0,
     Workload,
     bf16_bits_from_f32,
     build_host_cache,
@@ -20,4 +23,5 @@ from .generate import (  # noqa: F401
     encode_e4m3fn,
     make_workload,
     quantise_rows,
+    ue8m0_exponents,
 )

@@ -15,6 +15,18 @@ Required").  The group scale is amax/448 in fp32, the quantisation used by the
 synthetic workloads (the deployed model's power-of-two UE8M0 scales are a
 different format).
 
+Row format 1 (UE8M0 scales, 584-byte stride), the deployed model's scale
+format ("Input Knowledge Required" of the same page: unsigned 8-bit
+exponent-only scales, one per 64-column group):
+
+    bytes   0..447  448 fp8 e4m3fn codes
+    bytes 448..454  7 UE8M0 group scales (byte e stands for 2^(e - 127))
+    byte  455       8th scale slot: padding (0xFF)
+    bytes 456..583  64 rope values as bf16
+
+Its group scale is the smallest power of two s >= amax/448, so no code
+saturates.
+
 Every cache row that no top-k entry selects, and every row past a sequence's
 length, is 0xFF bytes, which decodes as NaN in fp8, bf16 and fp32: a kernel
 that reads a row it should not read produces NaN.
@@ -31,6 +43,11 @@ import math
 import numpy as np
 
 ROW_BYTES = 640
+ROW_FMT_FP32 = 0
+ROW_FMT_UE8M0 = 1
+ROW_BYTES_OF_FORMAT = {ROW_FMT_FP32: 640, ROW_FMT_UE8M0: 584}
+UE8M0_SCALE_OFF = 448
+UE8M0_ROPE_OFF = 456
 NOPE = 448
 ROPE = 64
 LATENT = NOPE + ROPE
@@ -80,13 +97,35 @@ def encode_e4m3fn(v: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def quantise_rows(nope: np.ndarray, rope: np.ndarray) -> np.ndarray:
-    """Pack fp32 nope [N,448] and rope [N,64] into cache rows uint8 [N,640]."""
+def ue8m0_exponents(amax: np.ndarray) -> np.ndarray:
+    """Exponent bytes e of the smallest powers of two 2^(e-127) >= amax/448
+    (e = 127 when amax is 0), clamped to [1, 254]."""
+    r = np.asarray(amax, dtype=np.float64) / FP8_MAX
+    f, k = np.frexp(r)                        # r = f * 2**k, f in [0.5, 1)
+    up = np.where(f == 0.5, k - 1, k)         # ceil(log2 r)
+    e = np.where(r == 0, 127, np.clip(up + 127, 1, 254))
+    return e.astype(np.uint8)
+
+
+def quantise_rows(nope: np.ndarray, rope: np.ndarray, row_format: int = ROW_FMT_FP32) -> np.ndarray:
+    """Pack fp32 nope [N,448] and rope [N,64] into cache rows uint8
+    [N, row bytes of the format]."""
     nope = np.ascontiguousarray(nope, dtype=np.float32)
     rope = np.ascontiguousarray(rope, dtype=np.float32)
     n = nope.shape[0]
     g = nope.reshape(n, NGROUPS, GROUP)
     amax = np.abs(g).max(axis=2)                                   # [N,7] fp32
+    if row_format == ROW_FMT_UE8M0:
+        e = ue8m0_exponents(amax)                                  # [N,7]
+        scale = np.ldexp(np.float32(1.0), e.astype(np.int32) - 127).astype(np.float32)
+        ratio = (g / scale[:, :, None]).astype(np.float32)         # exact: division by 2^k
+        codes = encode_e4m3fn(ratio).reshape(n, NOPE)
+        rows = np.full((n, ROW_BYTES_OF_FORMAT[ROW_FMT_UE8M0]), 0xFF, dtype=np.uint8)
+        rows[:, :NOPE] = codes
+        rows[:, UE8M0_SCALE_OFF:UE8M0_SCALE_OFF + NGROUPS] = e
+        rows[:, UE8M0_ROPE_OFF:UE8M0_ROPE_OFF + 2 * ROPE] = \
+            bf16_bits_from_f32(rope).view(np.uint8).reshape(n, 2 * ROPE)
+        return rows
     scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
     scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
     ratio = (g / scale[:, :, None]).astype(np.float32)             # fp32 x / s
@@ -114,8 +153,13 @@ class Workload:
     seqlens: np.ndarray       # int32 [B]
     idx: np.ndarray           # int32 [B, topk]; -1 = padding
     q_bits: np.ndarray        # uint16 [B, H, 512] bf16 bit patterns
-    rows: np.ndarray          # uint8 [B, topk, 640]: row of entry (b, j)
+    rows: np.ndarray          # uint8 [B, topk, row bytes]: row of entry (b, j)
     nsplits: tuple = (1,)     # split counts the parity tests use
+    row_format: int = ROW_FMT_FP32
+
+    @property
+    def row_bytes(self) -> int:
+        return ROW_BYTES_OF_FORMAT[self.row_format]
 
     @property
     def valid(self) -> np.ndarray:
@@ -156,7 +200,7 @@ def _draw_idx(rng, seqlens, topk, structure):
 
 def make_workload(*, name="custom", seed=0, batch, heads, topk, seqlen=None,
                   seqlens=None, kv_seq_stride=None, structure="uniform",
-                  q_mult=1.0, scale=None, nsplits=(1,)) -> Workload:
+                  q_mult=1.0, scale=None, nsplits=(1,), row_format=ROW_FMT_FP32) -> Workload:
     rng = np.random.Generator(np.random.PCG64(seed))
     if seqlens is None:
         seqlens = np.full(batch, seqlen, dtype=np.int32)
@@ -168,13 +212,13 @@ def make_workload(*, name="custom", seed=0, batch, heads, topk, seqlen=None,
     q = rng.standard_normal((batch, heads, LATENT), dtype=np.float32) * np.float32(q_mult)
     nope = rng.standard_normal((batch * topk, NOPE), dtype=np.float32)
     rope = rng.standard_normal((batch * topk, ROPE), dtype=np.float32)
-    rows = quantise_rows(nope, rope).reshape(batch, topk, ROW_BYTES)
+    rows = quantise_rows(nope, rope, row_format).reshape(batch, topk, ROW_BYTES_OF_FORMAT[row_format])
     if scale is None:
         scale = float(np.float32(1.0 / math.sqrt(LATENT)))
     return Workload(name=name, seed=seed, batch=batch, heads=heads, topk=topk,
                     kv_seq_stride=int(kv_seq_stride), scale=float(np.float32(scale)),
                     seqlens=seqlens, idx=idx, q_bits=bf16_bits_from_f32(q),
-                    rows=rows, nsplits=tuple(nsplits))
+                    rows=rows, nsplits=tuple(nsplits), row_format=row_format)
 
 
 def _cfg5_seqlens(seed):
@@ -202,16 +246,20 @@ CONFIGS = {
 }
 
 
-def config_workload(cfg: int) -> Workload:
+def config_workload(cfg: int, row_format: int = ROW_FMT_FP32) -> Workload:
+    """Workload number cfg; with row_format 1 the same shapes and draws in the
+    UE8M0 row format (its name gets a _ue8m0 suffix)."""
     c = dict(CONFIGS[cfg])
     if c.get("seqlens") == "cfg5":
         c["seqlens"] = _cfg5_seqlens(cfg)
-    return make_workload(seed=cfg, **c)
+    if row_format == ROW_FMT_UE8M0:
+        c["name"] = c["name"] + "_ue8m0"
+    return make_workload(seed=cfg, row_format=row_format, **c)
 
 
 def build_host_cache(w: Workload) -> np.ndarray:
-    """Full cache uint8 [B, kv_seq_stride, 640]: selected rows placed, rest 0xFF."""
-    cache = np.full((w.batch, w.kv_seq_stride, ROW_BYTES), 0xFF, dtype=np.uint8)
+    """Full cache uint8 [B, kv_seq_stride, row bytes]: selected rows placed, rest 0xFF."""
+    cache = np.full((w.batch, w.kv_seq_stride, w.row_bytes), 0xFF, dtype=np.uint8)
     v = w.valid
     b_i, j_i = np.nonzero(v)
     cache[b_i, w.idx[b_i, j_i]] = w.rows[b_i, j_i]
