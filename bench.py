@@ -16,8 +16,9 @@ time the whole loop.  A second timed loop of K decode-kernel launches alone
 gives that kernel's average duration for the roofline.
 
 Prints one JSON line with queries*heads/s, effective KV GB/s, the roofline
-object of the decode kernel (algorithmic KV bytes = 604 per kept row), and
-the fp64 CPU oracle timed on the host as a baseline.
+object of the decode kernel (algorithmic KV bytes = 604 per kept row with fp32
+group scales, 583 with UE8M0 scale bytes), and the fp64 CPU oracle timed on
+the host as a baseline.
 """
 
 from __future__ import annotations
@@ -39,7 +40,9 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-MLA decode queries·heads/s + effective KV GB/s (% of MI355X roofline)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA
-ROW_ALGO_BYTES = 604            # 448 fp8 + 7 fp32 scales + 64 bf16 rope per kept row
+# bytes of a kept row the decode must read: 448 fp8 codes + 7 group scales
+# (fp32, or one byte each in the UE8M0 format) + 64 bf16 rope values
+ROW_ALGO_BYTES = {0: 448 + 7 * 4 + 128, 1: 448 + 7 + 128}
 
 
 def log(*a):
@@ -50,12 +53,12 @@ COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "decode_b32_h64_s32768_k512_ker
 COUNTER_CONFIG = 3
 
 
-def counted_traffic(config):
+def counted_traffic(config, row_format):
     """HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE, calibrated against a
     plain device copy) from the committed rocprofv3 counter summary, when that
     summary was taken on this workload and on the current kernel source; None
     otherwise."""
-    if config != COUNTER_CONFIG or not os.path.exists(COUNTER_SUMMARY):
+    if config != COUNTER_CONFIG or row_format != 0 or not os.path.exists(COUNTER_SUMMARY):
         return None
     text = open(COUNTER_SUMMARY).read()
     src = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc", "smla.hip")
@@ -74,6 +77,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=3, help="workload number 1..5 (default 3)")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--row-format", type=int, default=0, choices=(0, 1),
+                    help="cache rows: 0 = fp32 group scales (640 B), 1 = UE8M0 scale bytes (584 B)")
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto, > 768 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -95,7 +100,7 @@ def main():
     import torch
 
     import sparse_mla_decode_02_amd as smla
-    from workloads import CONFIGS, ROW_BYTES, config_workload
+    from workloads import config_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -103,22 +108,23 @@ def main():
     stream = torch.cuda.current_stream()
 
     t0 = time.time()
-    w = config_workload(args.config)
+    w = config_workload(args.config, row_format=args.row_format)
     B, H, K = w.batch, w.heads, w.topk
+    RB, fmt = w.row_bytes, w.row_format
     valid = w.valid
     n_rows = int(valid.sum())
     log(f"workload {w.name}: B={B} H={H} topk={K} stride={w.kv_seq_stride} kept rows={n_rows} "
         f"(generated in {time.time() - t0:.1f}s)")
 
-    ns = smla.num_splits(B, H, K, args.num_splits, w.kv_seq_stride)
-    chunk = smla.split_size(B, H, K, args.num_splits, w.kv_seq_stride)
+    ns = smla.num_splits(B, H, K, args.num_splits, w.kv_seq_stride, fmt)
+    chunk = smla.split_size(B, H, K, args.num_splits, w.kv_seq_stride, fmt)
 
     # ---- device inputs: R rotating copies
     b_i, j_i = np.nonzero(valid)
     flat = torch.from_numpy(b_i.astype(np.int64) * w.kv_seq_stride + w.idx[b_i, j_i]).to(dev)
     rows = torch.from_numpy(np.ascontiguousarray(w.rows[b_i, j_i])).to(dev)
-    step_bytes = n_rows * ROW_BYTES + B * H * 512 * 2 * 2 + B * K * 4
-    cache_bytes = B * w.kv_seq_stride * ROW_BYTES
+    step_bytes = n_rows * RB + B * H * 512 * 2 * 2 + B * K * 4
+    cache_bytes = B * w.kv_seq_stride * RB
     if args.warm:
         R = 1
     elif args.rotate > 0:
@@ -131,8 +137,8 @@ def main():
     idx0 = torch.from_numpy(w.idx).to(dev)
     sl0 = torch.from_numpy(w.seqlens).to(dev)
     for r in range(R):
-        cache = torch.full((B, w.kv_seq_stride, ROW_BYTES), 0xFF, dtype=torch.uint8, device=dev)
-        cache.view(-1, ROW_BYTES)[flat] = rows
+        cache = torch.full((B, w.kv_seq_stride, RB), 0xFF, dtype=torch.uint8, device=dev)
+        cache.view(-1, RB)[flat] = rows
         sets.append((q0.clone(), cache, idx0.clone(), sl0.clone()))
     out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
@@ -146,12 +152,12 @@ def main():
     # is a single ctypes call (the host must stay ahead of the GPU).
     import ctypes
     L = smla.lib()
-    shape = smla.make_shape(B, H, K, args.num_splits, w.kv_seq_stride)
+    shape = smla.make_shape(B, H, K, args.num_splits, w.kv_seq_stride, fmt)
     hs = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     dec_args, full_args = [], []
     ws = None
-    need_ws = smla.workspace_bytes(B, H, K, args.num_splits, w.kv_seq_stride)
+    need_ws = smla.workspace_bytes(B, H, K, args.num_splits, w.kv_seq_stride, fmt)
     if need_ws:
         ws = torch.empty(need_ws, dtype=torch.uint8, device=dev)
     for q, cache, idx, sl in sets:
@@ -209,7 +215,7 @@ def main():
     dec_ms, _ = timed(decode_only, args.steps)
     comb_ms = ms_per_step - dec_ms if ns > 1 else 0.0
     t_dec = dec_ms * 1e-3
-    kv_bytes = ROW_ALGO_BYTES * n_rows
+    kv_bytes = ROW_ALGO_BYTES[fmt] * n_rows
     all_bytes = kv_bytes + B * H * 512 * 2 * 2 + B * H * 4 + B * K * 4 + B * 4
     kv_gbps = kv_bytes / t_dec / 1e9
     flops = 2048.0 * H * n_rows
@@ -226,7 +232,8 @@ def main():
         reps, t_cpu, used = 0, 0.0, 0
         while t_cpu < args.cpu_seconds and reps < 1000:
             c0 = time.perf_counter()
-            _, _, used = oracle.decode_raw(w.q_bits, hc, w.kv_seq_stride, w.idx, w.seqlens, H, w.scale)
+            _, _, used = oracle.decode_raw(w.q_bits, hc, w.kv_seq_stride, w.idx, w.seqlens, H, w.scale,
+                                           row_format=fmt)
             t_cpu += time.perf_counter() - c0
             reps += 1
         del hc
@@ -252,9 +259,10 @@ def main():
         "config": {"workload": w.name, "config_number": args.config, "batch": B, "heads": H,
                    "topk": K, "seq_len": int(w.kv_seq_stride), "kept_rows": n_rows,
                    "num_splits": ns, "split_size": chunk, "rotation": R,
+                   "row_format": "ue8m0_scales_584B" if fmt == 1 else "fp32_scales_640B",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": counted_traffic(args.config)},
+                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": counted_traffic(args.config, fmt)},
         "cpu_baseline": cpu,
         "effective_kv_gbps": kv_gbps,
         "all_algorithmic_gbps": all_bytes / t_dec / 1e9,

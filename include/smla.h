@@ -5,7 +5,8 @@
  * (one per sequence) attends, with all of this GPU's heads, over the latent KV
  * rows that the sequence's top-k list selects.  Keys and values are the same
  * 512-wide latent row: 448 "nope" columns stored as fp8 e4m3fn codes with one
- * fp32 scale per 64-column group, and 64 "rope" columns stored as bf16.
+ * scale per 64-column group (fp32, or an exponent byte), and 64 "rope" columns
+ * stored as bf16.
  * Sources: "The Moment of Compilation", section "The Context: A Kernel
  * Optimization Campaign" (one KV read shared by all heads in a batched
  * matrix product); "The Power-of-Two Trap", sections "The Scene", "The Scale
@@ -31,26 +32,42 @@
 extern "C" {
 #endif
 
-/* Cache row format: one token's latent row, SMLA_ROW_BYTES apart.
+/* Cache row formats: one token's latent row, a fixed number of bytes apart.
+ *
+ * SMLA_ROW_FP32_SCALES (0), SMLA_ROW_BYTES = 640 bytes per row:
  *   bytes   0..447  nope, 448 fp8 e4m3fn codes (OCP, largest finite 448)
  *   bytes 448..479  8 fp32 group scales; slot g scales nope columns 64g..64g+63
  *                   for g < 7; slot 7 is padding, its value is never used
  *   bytes 480..607  rope, 64 bf16 values
  *   bytes 608..639  padding, never read
- * Dequantised row: K[i] = e4m3(code[i]) * scale[i / 64] for i < 448,
- *                  K[448 + k] = rope[k]. */
+ *
+ * SMLA_ROW_UE8M0_SCALES (1), SMLA_ROW_BYTES_UE8M0 = 584 bytes per row: the
+ * exponent-only scale format ("The Power-of-Two Trap", section "Input
+ * Knowledge Required": unsigned 8-bit scale exponents, one per 64 columns):
+ *   bytes   0..447  nope, 448 fp8 e4m3fn codes
+ *   bytes 448..454  7 group scale bytes; byte e stands for 2^(e - 127)
+ *                   (e = 255 is NaN)
+ *   byte  455       padding, never read
+ *   bytes 456..583  rope, 64 bf16 values
+ *
+ * Dequantised row (both formats): K[i] = e4m3(code[i]) * scale[i / 64] for
+ * i < 448, K[448 + k] = rope[k]. */
+#define SMLA_ROW_FP32_SCALES 0
+#define SMLA_ROW_UE8M0_SCALES 1
 #define SMLA_ROW_BYTES 640
+#define SMLA_ROW_BYTES_UE8M0 584
 #define SMLA_NOPE_DIM 448
 #define SMLA_ROPE_DIM 64
 #define SMLA_LATENT_DIM 512
 #define SMLA_GROUP 64
 #define SMLA_SCALE_OFFSET 448
 #define SMLA_ROPE_OFFSET 480
+#define SMLA_ROPE_OFFSET_UE8M0 456
 
 typedef enum {
     SMLA_OK = 0,
     SMLA_ERR_NULL = 1,         /* a required pointer is NULL */
-    SMLA_ERR_SHAPE = 2,        /* bad batch/heads/topk/splits/stride */
+    SMLA_ERR_SHAPE = 2,        /* bad batch/heads/topk/splits/stride/row format */
     SMLA_ERR_UNSUPPORTED = 3,  /* current device is not gfx950 */
     SMLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
     SMLA_ERR_HIP = 5,          /* a HIP runtime call or launch failed */
@@ -63,7 +80,9 @@ typedef struct {
     int32_t num_heads;      /* H >= 0, multiple of 16, <= 256: this GPU's heads */
     int32_t topk;           /* >= 0: entries in each top-k list */
     int32_t num_splits;     /* >= 0: split-K chunks per list; 0 = library's choice */
-    int64_t kv_seq_stride;  /* >= 1: cache rows between sequence b and b + 1 */
+    int64_t kv_seq_stride;  /* >= 1: cache rows between sequence b and b + 1;
+                               kv_seq_stride * row bytes must be below 2^31 */
+    int32_t row_format;     /* SMLA_ROW_FP32_SCALES (0) or SMLA_ROW_UE8M0_SCALES (1) */
 } smla_shape;
 
 /* Split count a call with this shape uses (num_splits == 0 resolved by the
@@ -80,8 +99,9 @@ size_t smla_workspace_bytes(const smla_shape* shape);
  * sparse_mla_decode -- one decode step.
  *
  *   q         bf16 [B][H][512], 16-byte aligned; columns 0..447 nope, 448..511 rope
- *   kv_cache  bytes [B][kv_seq_stride][640] (row format above), 16-byte aligned;
- *             row t of sequence b starts at (b * kv_seq_stride + t) * 640
+ *   kv_cache  bytes [B][kv_seq_stride][R] in shape->row_format (R = 640 or
+ *             584, formats above), 16-byte aligned; row t of sequence b
+ *             starts at (b * kv_seq_stride + t) * R
  *   topk_idx  int32 [B][topk], 4-byte aligned: cache row of each list entry.
  *             An entry is skipped when it is < 0 or >= seqlens[b] (-1 pads
  *             short lists); entries may come in any order; a repeated entry
@@ -106,8 +126,9 @@ size_t smla_workspace_bytes(const smla_shape* shape);
  * Numerical contract: q . K is accumulated in fp32 from the exact bf16 query
  * and exact fp8/bf16 key values, with the group scales applied in fp32; the
  * softmax weights enter the value product in fp16 (value codes exact), so
- * group scales must be finite and below 256 and rope values below 65504 in
- * magnitude.  NaN inputs propagate to the affected outputs.
+ * group scales must be finite and below 256 (UE8M0 bytes at most 134) and
+ * rope values below 65504 in magnitude.  NaN inputs propagate to the
+ * affected outputs.
  */
 smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* topk_idx,
                               const int32_t* seqlens, float scale, void* out, float* lse,

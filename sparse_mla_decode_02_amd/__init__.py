@@ -16,6 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsmla.so")
 
 SMLA_OK = 0
+ROW_FP32_SCALES = 0          # SMLA_ROW_FP32_SCALES: 640-byte rows, fp32 group scales
+ROW_UE8M0_SCALES = 1         # SMLA_ROW_UE8M0_SCALES: 584-byte rows, exponent-byte scales
+ROW_BYTES_OF_FORMAT = {ROW_FP32_SCALES: 640, ROW_UE8M0_SCALES: 584}
 ROW_BYTES = 640
 LATENT = 512
 NOPE = 448
@@ -33,7 +36,7 @@ EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combin
 class SmlaShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-                ("kv_seq_stride", ctypes.c_int64)]
+                ("kv_seq_stride", ctypes.c_int64), ("row_format", ctypes.c_int32)]
 
 
 class SmlaError(RuntimeError):
@@ -81,23 +84,32 @@ def _check(status: int):
         raise SmlaError(status, status_str(status))
 
 
-def make_shape(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> SmlaShape:
-    return SmlaShape(int(batch), int(num_heads), int(topk), int(num_splits), int(kv_seq_stride))
+def make_shape(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> SmlaShape:
+    return SmlaShape(int(batch), int(num_heads), int(topk), int(num_splits), int(kv_seq_stride),
+                     int(row_format))
 
 
-def num_splits(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> int:
-    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride)
+def num_splits(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> int:
+    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride, row_format)
     return int(lib().smla_num_splits(ctypes.byref(s)))
 
 
-def split_size(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> int:
-    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride)
+def split_size(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> int:
+    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride, row_format)
     return int(lib().smla_split_size(ctypes.byref(s)))
 
 
-def workspace_bytes(batch, num_heads, topk, num_splits=0, kv_seq_stride=1) -> int:
-    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride)
+def workspace_bytes(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> int:
+    s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride, row_format)
     return int(lib().smla_workspace_bytes(ctypes.byref(s)))
+
+
+def _seq_stride(kv_cache, B, row_format):
+    if kv_cache is None:
+        return 1
+    if kv_cache.dim() == 3:
+        return kv_cache.shape[1]
+    return kv_cache.numel() // (max(B, 1) * ROW_BYTES_OF_FORMAT.get(row_format, ROW_BYTES))
 
 
 def _stream_handle(stream):
@@ -112,10 +124,11 @@ def _ptr(t):
 
 
 def sparse_mla_decode(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, num_splits=0,
-                      kv_seq_stride=None, workspace=None, stream=None):
+                      kv_seq_stride=None, workspace=None, stream=None, row_format=0):
     """One decode step through libsmla.so.
 
-    q: bf16 [B,H,512]; kv_cache: uint8 [B, kv_seq_stride, 640] (or flat);
+    q: bf16 [B,H,512]; kv_cache: uint8 [B, kv_seq_stride, R] (or flat), R =
+    640 for row_format 0 (fp32 scales) or 584 for row_format 1 (UE8M0 scales);
     topk_idx: int32 [B,topk]; seqlens: int32 [B]; out: bf16 [B,H,512];
     lse: float32 [B,H]; workspace: uint8 device tensor of at least
     workspace_bytes(...) bytes, allocated here when None.
@@ -124,8 +137,8 @@ def sparse_mla_decode(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, num_sp
     B, H, _ = q.shape
     topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
     if kv_seq_stride is None:
-        kv_seq_stride = kv_cache.shape[1] if kv_cache.dim() == 3 else kv_cache.numel() // (max(B, 1) * ROW_BYTES)
-    shape = make_shape(B, H, topk, num_splits, kv_seq_stride)
+        kv_seq_stride = _seq_stride(kv_cache, B, row_format)
+    shape = make_shape(B, H, topk, num_splits, kv_seq_stride, row_format)
     L = lib()
     need = int(L.smla_workspace_bytes(ctypes.byref(shape)))
     if workspace is None and need > 0:
@@ -138,13 +151,13 @@ def sparse_mla_decode(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, num_sp
 
 
 def sparse_mla_decode_partials(q, kv_cache, topk_idx, seqlens, scale, o_part, lse_part, *,
-                               num_splits=0, kv_seq_stride=None, stream=None):
+                               num_splits=0, kv_seq_stride=None, stream=None, row_format=0):
     """Decode kernel only: per-split partials o_part fp32 [B,H,S,512], lse_part fp32 [B,H,S]."""
     B, H, _ = q.shape
     topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
     if kv_seq_stride is None:
-        kv_seq_stride = kv_cache.shape[1]
-    shape = make_shape(B, H, topk, num_splits, kv_seq_stride)
+        kv_seq_stride = _seq_stride(kv_cache, B, row_format)
+    shape = make_shape(B, H, topk, num_splits, kv_seq_stride, row_format)
     _check(lib().sparse_mla_decode_partials(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(seqlens),
                                             ctypes.c_float(scale), ctypes.byref(shape), _ptr(o_part),
                                             _ptr(lse_part), _stream_handle(stream)))

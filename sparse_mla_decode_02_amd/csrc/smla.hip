@@ -53,7 +53,6 @@
 
 namespace {
 
-constexpr int kRowBytes = SMLA_ROW_BYTES;   // 640
 constexpr int kNope = SMLA_NOPE_DIM;        // 448
 constexpr int kLatent = SMLA_LATENT_DIM;    // 512
 constexpr int kTile = 32;                   // tokens per tile
@@ -82,6 +81,7 @@ typedef __attribute__((address_space(3))) const float lds_cf32;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef __attribute__((address_space(3))) const int32_t lds_ci32;
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
 
 // LDS tile slot.  The 36 16-byte pieces of a row (0..27 the fp8 codes, 28..35
 // the rope) are stored in 18 blocks of 1 KB: block 2j + hh holds pieces
@@ -105,6 +105,27 @@ constexpr int kAccBytes = 32 * 64 * 16;               // one wave's output accum
 constexpr int kWaveLds = 2 * kSlot;                   // two tile slots per wave
 constexpr int kStat = kWaves * kAccBytes;             // merge statistics, after the merge buffers
 constexpr int kLdsBytes = kWaves * kWaveLds;          // 152 KB
+
+// Byte layout of a cache row in each format (include/smla.h).  Both keep the
+// codes at 0..447 and the scales at 448; the rope follows the scales.
+template <int F>
+struct RowFormat;
+template <>
+struct RowFormat<SMLA_ROW_FP32_SCALES> {
+    static constexpr int kBytes = SMLA_ROW_BYTES;        // 640
+    static constexpr int kRopeOff = SMLA_ROPE_OFFSET;    // 480
+};
+template <>
+struct RowFormat<SMLA_ROW_UE8M0_SCALES> {
+    static constexpr int kBytes = SMLA_ROW_BYTES_UE8M0;      // 584
+    static constexpr int kRopeOff = SMLA_ROPE_OFFSET_UE8M0;  // 456
+};
+
+// UE8M0 rows: the tile's 7 scale bytes per row are first gathered as two
+// dwords per position (lane l: bytes 448 + 4 (l >> 5) .. + 3 of the row in
+// position l & 31) into rows 4 and 5 of the scale table, then expanded in place
+// into the fp32 table rows 0..6 before the tile is computed.
+constexpr int kScaleRaw = kScaleTable + 4 * kTile * 4;
 
 static_assert(kStat + kWaves * 32 * 4 <= kLdsBytes, "merge buffers and statistics reuse the slots");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
@@ -209,10 +230,12 @@ __device__ __forceinline__ i32x4 row_rsrc(const uint8_t* base, uint32_t bytes) {
     return r;
 }
 
-// Byte offset of byte `off` of cache row `row` (row in [-1, 2^23)), modulo 2^32.
-// Row -1 gives an offset above 2^32 - 640, out of range for every sequence.
+// Byte offset of byte `off` (< row bytes) of cache row `row` (row in
+// [-1, 2^23)) in format F, modulo 2^32.  Row -1 gives an offset above 2^32 minus
+// the row bytes, out of range for every sequence.
+template <int F>
 __device__ __forceinline__ uint32_t row_offset(int row, uint32_t off) {
-    return (uint32_t)__mul24(row, kRowBytes) + off;
+    return (uint32_t)__mul24(row, RowFormat<F>::kBytes) + off;
 }
 
 // 4-byte gather of one lane straight into LDS at lds_base + 4 * lane:
@@ -290,64 +313,94 @@ struct DecodeArgs {
     float* o_part;
     float* lse_part;
     int64_t kv_seq_stride;
-    uint32_t seq_bytes;   // kv_seq_stride * 640 (< 2^31): the range of a sequence's rows
+    uint32_t seq_bytes;   // kv_seq_stride * row bytes (< 2^31): the range of a sequence's rows
     float logit_factor;   // scale * log2(e)
     int32_t batch, heads, topk, nsplit, chunk, n_hb;
     int32_t force_partials;   // write split partials even when nsplit == 1
     int32_t xcd_remap;        // grid is a multiple of 8: keep a sequence's blocks on one XCD
+    int32_t row_format;       // host only: selects the kernel instance
 };
 
 // Gather one whole 32-token tile into the LDS slot at slot_lds.  Lane l holds
 // the (sanitised) row of LDS position l & 31.  Block gather 2j + hh: lane l
 // loads the 16 bytes that belong at chunk l & 3 of position 16hh + (l >> 2),
 // i.e. piece 4j + ((l & 3) ^ ((l >> 4) & 3)) of that position's row, from
-// source byte 16 * piece (codes) or 16 * piece + 32 (rope; the scales sit
-// between them in the cache row).  The two rows each lane needs come from the
-// lanes holding them (2 ds_bpermute per tile), and the 18 gathers share two
-// offset registers.  Scale gather k loads scale 2k + (l >> 5) of position
-// l & 31 into row 2k + (l >> 5) of the table; the last one leaves out group 7
-// (padding), whose row holds list entries instead (see load_entries_lds).
+// source byte 16 * piece (codes) or 16 * piece + rope offset - 448 (rope; the
+// scales sit between them in the cache row).  The two rows each lane needs come
+// from the lanes holding them (2 ds_bpermute per tile), and the 18 gathers share
+// two offset registers.  fp32 scales: scale gather k loads scale 2k + (l >> 5) of
+// position l & 31 into row 2k + (l >> 5) of the table; the last one leaves out
+// group 7 (padding), whose row holds list entries instead (see
+// load_entries_lds).  UE8M0 scales: one gather of 4 bytes per lane (see
+// kScaleRaw).
 struct TileGather {
     uint32_t v0, v1;     // source offsets for the blocks of positions 0..15 and 16..31
     uint32_t vscale;     // source offset of this lane's scale pair
     uint32_t slot;       // LDS slot address
 };
 
+template <int F>
 __device__ __forceinline__ TileGather plan_tile(int row, uint32_t slot_lds, int lane) {
     const int row0 = __builtin_amdgcn_ds_bpermute(4 * (lane >> 2), row);
     const int row1 = __builtin_amdgcn_ds_bpermute(4 * (16 + (lane >> 2)), row);
     const uint32_t pp = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     TileGather g;
-    g.v0 = row_offset(row0, 16u * pp);
-    g.v1 = row_offset(row1, 16u * pp);
-    g.vscale = row_offset(row, SMLA_SCALE_OFFSET + 4u * ((uint32_t)lane >> 5));
+    g.v0 = row_offset<F>(row0, 16u * pp);
+    g.v1 = row_offset<F>(row1, 16u * pp);
+    g.vscale = row_offset<F>(row, SMLA_SCALE_OFFSET + 4u * ((uint32_t)lane >> 5));
     g.slot = slot_lds;
     return g;
 }
 
+template <int F>
 __device__ __forceinline__ void issue_scales(const TileGather& g, i32x4 rsrc, int lane) {
-    static_for<0, kScaleGathers - 1>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        gather4_at<8 * k>(g.vscale, rsrc, g.slot + kScaleTable + 256 * k);
-    });
-    if (lane < 32) gather4_at<8 * (kScaleGathers - 1)>(g.vscale, rsrc, g.slot + kScaleTable + 256 * (kScaleGathers - 1));
+    if constexpr (F == SMLA_ROW_UE8M0_SCALES) {
+        gather4_at<0>(g.vscale, rsrc, g.slot + kScaleRaw);
+    } else {
+        static_for<0, kScaleGathers - 1>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            gather4_at<8 * k>(g.vscale, rsrc, g.slot + kScaleTable + 256 * k);
+        });
+        if (lane < 32)
+            gather4_at<8 * (kScaleGathers - 1)>(g.vscale, rsrc, g.slot + kScaleTable + 256 * (kScaleGathers - 1));
+    }
 }
 
 // Blocks 2j and 2j + 1 for j in [J0, J1).
-template <int J0, int J1>
+template <int F, int J0, int J1>
 __device__ __forceinline__ void issue_blocks(const TileGather& g, i32x4 rsrc) {
     static_for<J0, J1>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        constexpr int off = 64 * j + (4 * j >= kCodePieces ? 32 : 0);
+        constexpr int off = 64 * j + (4 * j >= kCodePieces ? RowFormat<F>::kRopeOff - SMLA_SCALE_OFFSET : 0);
         gather16_at<off>(g.v0, rsrc, g.slot + 1024 * (2 * j));
         gather16_at<off>(g.v1, rsrc, g.slot + 1024 * (2 * j + 1));
     });
 }
 
+template <int F>
 __device__ __forceinline__ void issue_tile(int row, i32x4 rsrc, uint32_t slot_lds, int lane) {
-    const TileGather g = plan_tile(row, slot_lds, lane);
-    issue_scales(g, rsrc, lane);
-    issue_blocks<0, kRowGathers / 2>(g, rsrc);
+    const TileGather g = plan_tile<F>(row, slot_lds, lane);
+    issue_scales<F>(g, rsrc, lane);
+    issue_blocks<F, 0, kRowGathers / 2>(g, rsrc);
+}
+
+// Value 2^(e - 127) of a UE8M0 scale byte as fp32: the exponent field alone,
+// except 0 (2^-127, a subnormal) and 255 (NaN).
+__device__ __forceinline__ float ue8m0_value(uint32_t e) {
+    const uint32_t bits = e == 0 ? 0x00400000u : e == 255 ? 0x7FC00000u : e << 23;
+    return __uint_as_float(bits);
+}
+
+// Expands the gathered UE8M0 bytes of a landed tile into its fp32 scale table
+// (rows 0..6; row 7 holds list entries).  Lane l holds bytes of groups
+// 4 (l >> 5) .. + 3 of position l & 31; its one LDS read precedes the writes,
+// which overwrite the raw dwords.
+__device__ __forceinline__ void expand_ue8m0_scales(lds_u8* st, int lane) {
+    const uint32_t d = ((lds_cu32*)(st + kScaleRaw))[lane];
+    lds_f32* sT = (lds_f32*)(st + kScaleTable) + 4 * kTile * (lane >> 5) + (lane & 31);
+#pragma unroll
+    for (int k = 0; k < 3; k++) sT[k * kTile] = ue8m0_value((d >> (8 * k)) & 0xFFu);
+    if (lane < 32) sT[3 * kTile] = ue8m0_value(d >> 24);
 }
 
 // Position of the list entries of a tile in an LDS slot: the unused group-7
@@ -611,6 +664,7 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
 // each gathered into the wave's own two LDS slots one tile ahead), then merge
 // their online-softmax states once, through LDS, and write the split's
 // normalised output and log-sum-exp (or the final bf16 result).
+template <int F>
 __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
     lds_u8* const lds = (lds_u8*)lds_raw;
@@ -632,7 +686,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
     const int ntiles = (n_ent + kTile - 1) / kTile;
     const int seqlen = a.seqlens[b];
-    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * kRowBytes, a.seq_bytes);
+    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
     const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
 
     // ---- the query of this lane's head as the B operand of S^T = K . Q^T
@@ -686,7 +740,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         row_cur = sanitise(0, e0);
         row_1 = sanitise(1, e1);
         row_2 = sanitise(2, e2);
-        issue_tile(row_cur, rsrc, my_lds_addr, lane);
+        issue_tile<F>(row_cur, rsrc, my_lds_addr, lane);
     }
     // the query lands while the first tile is gathered
     load_query();
@@ -705,22 +759,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         const bool more = i + 1 < my_n;
         TileGather tg = {};
         if (more) {
-            tg = plan_tile(row_next, my_lds_addr + slot1 * kSlot, lane);
-            issue_scales(tg, rsrc, lane);
-            issue_blocks<0, 2>(tg, rsrc);
+            tg = plan_tile<F>(row_next, my_lds_addr + slot1 * kSlot, lane);
+            issue_scales<F>(tg, rsrc, lane);
+            issue_blocks<F, 0, 2>(tg, rsrc);
         }
         auto issue_part = [&](auto stage) {
             if (!more) return;
             constexpr int k = decltype(stage)::value;
             if constexpr (k == 0) {
-                issue_blocks<2, 6>(tg, rsrc);
+                issue_blocks<F, 2, 6>(tg, rsrc);
             } else if constexpr (k == 1) {
-                issue_blocks<6, kRowGathers / 2>(tg, rsrc);
+                issue_blocks<F, 6, kRowGathers / 2>(tg, rsrc);
                 if (i >= 1 && i + 2 < my_n)
                     load_entries_lds(first_entry(i + 2), idx_rsrc, my_lds_addr + (i & 1) * kSlot, lane);
             }
         };
         const uint64_t vmask = mask_by_token(__ballot(lane < kTile && row_cur >= 0));
+        if constexpr (F == SMLA_ROW_UE8M0_SCALES) expand_ue8m0_scales(my_lds + (i & 1) * kSlot, lane);
         compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor, issue_part);
         row_cur = row_next;
     }
@@ -795,13 +850,17 @@ struct Plan {
     int chunk;    // list entries per split (multiple of kTile)
 };
 
-// Rows of one sequence are addressed by 32-bit byte offsets below 2^31.
-constexpr int64_t kMaxSeqStride = ((int64_t)1 << 31) / kRowBytes;
+int row_bytes_of(int32_t fmt) {
+    return fmt == SMLA_ROW_FP32_SCALES ? SMLA_ROW_BYTES : fmt == SMLA_ROW_UE8M0_SCALES ? SMLA_ROW_BYTES_UE8M0 : 0;
+}
 
+// Rows of one sequence are addressed by 32-bit byte offsets below 2^31.
 bool shape_ok(const smla_shape* s) {
-    return s && s->batch >= 0 && s->num_heads >= 0 && s->num_heads % 16 == 0 &&
+    if (!s) return false;
+    const int rb = row_bytes_of(s->row_format);
+    return rb > 0 && s->batch >= 0 && s->num_heads >= 0 && s->num_heads % 16 == 0 &&
            s->num_heads <= 256 && s->topk >= 0 && s->num_splits >= 0 && s->kv_seq_stride >= 1 &&
-           s->kv_seq_stride <= kMaxSeqStride;
+           s->kv_seq_stride <= (((int64_t)1 << 31) - 1) / rb;
 }
 
 constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
@@ -955,7 +1014,8 @@ static smla_status prepare(const void* q, const void* kv_cache, const int32_t* t
     a->nsplit = p->nsplit;
     a->chunk = p->chunk;
     a->n_hb = p->n_hb;
-    a->seq_bytes = (uint32_t)(shape->kv_seq_stride * kRowBytes);
+    a->seq_bytes = (uint32_t)(shape->kv_seq_stride * row_bytes_of(shape->row_format));
+    a->row_format = shape->row_format;
     return SMLA_OK;
 }
 
@@ -963,7 +1023,10 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const int grid = a.batch * p.n_hb * p.nsplit;
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(smla_decode_kernel, dim3(grid), dim3(64 * kWaves), 0, hs, args);
+    if (a.row_format == SMLA_ROW_UE8M0_SCALES)
+        hipLaunchKernelGGL(smla_decode_kernel<SMLA_ROW_UE8M0_SCALES>, dim3(grid), dim3(64 * kWaves), 0, hs, args);
+    else
+        hipLaunchKernelGGL(smla_decode_kernel<SMLA_ROW_FP32_SCALES>, dim3(grid), dim3(64 * kWaves), 0, hs, args);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 

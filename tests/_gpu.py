@@ -9,7 +9,6 @@ import numpy as np
 import torch
 
 import sparse_mla_decode_02_amd as smla
-from workloads import ROW_BYTES
 
 
 def log(*a):
@@ -18,15 +17,15 @@ def log(*a):
 
 
 def device_inputs(w, dev="cuda:0"):
-    """q bf16 [B,H,512], cache uint8 [B,S,640] (0xFF except selected rows), idx, seqlens."""
+    """q bf16 [B,H,512], cache uint8 [B,S,row bytes] (0xFF except selected rows), idx, seqlens."""
     q = torch.from_numpy(w.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    cache = torch.full((w.batch, w.kv_seq_stride, ROW_BYTES), 0xFF, dtype=torch.uint8, device=dev)
+    cache = torch.full((w.batch, w.kv_seq_stride, w.row_bytes), 0xFF, dtype=torch.uint8, device=dev)
     valid = w.valid
     b_i, j_i = np.nonzero(valid)
     if len(b_i):
         flat = torch.from_numpy((b_i.astype(np.int64) * w.kv_seq_stride + w.idx[b_i, j_i]).astype(np.int64)).to(dev)
         rows = torch.from_numpy(np.ascontiguousarray(w.rows[b_i, j_i])).to(dev)
-        cache.view(-1, ROW_BYTES)[flat] = rows
+        cache.view(-1, w.row_bytes)[flat] = rows
     idx = torch.from_numpy(w.idx).to(dev)
     seqlens = torch.from_numpy(w.seqlens).to(dev)
     return q, cache, idx, seqlens
@@ -38,12 +37,12 @@ def run_decode(w, inputs=None, num_splits=0, poison_workspace=True, idx=None):
     B, H = w.batch, w.heads
     out = torch.full((B, H, 512), float("nan"), dtype=torch.bfloat16, device=q.device)
     lse = torch.full((B, H), float("nan"), dtype=torch.float32, device=q.device)
-    need = smla.workspace_bytes(B, H, idx.shape[1], num_splits, w.kv_seq_stride)
+    need = smla.workspace_bytes(B, H, idx.shape[1], num_splits, w.kv_seq_stride, w.row_format)
     ws = None
     if need:
         ws = torch.full((need,), 0xFF if poison_workspace else 0, dtype=torch.uint8, device=q.device)
     smla.sparse_mla_decode(q, cache, idx, seqlens, w.scale, out, lse, num_splits=num_splits,
-                           kv_seq_stride=w.kv_seq_stride, workspace=ws)
+                           kv_seq_stride=w.kv_seq_stride, workspace=ws, row_format=w.row_format)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

@@ -89,6 +89,8 @@ def test_argument_errors_before_any_device_work():
     assert _call(L, smla.make_shape(-1, 16, 64, 1, 128)) == 2     # negative batch
     assert _call(L, smla.make_shape(2, 16, 64, -2, 128)) == 2     # negative splits
     assert _call(L, smla.make_shape(2, 16, 64, 1, 0)) == 2        # stride < 1
+    assert _call(L, smla.make_shape(2, 16, 64, 1, 128, 2)) == 2   # unknown row format
+    assert _call(L, smla.make_shape(2, 16, 64, 1, 128, -1)) == 2
     assert _call(L, good, {"q": ctypes.c_void_p((1 << 20) + 4)}) == 6   # q misaligned
     assert _call(L, good, {"idx": ctypes.c_void_p((1 << 20) + 2)}) == 6  # idx misaligned
     split = smla.make_shape(2, 16, 64, 2, 128)
@@ -119,3 +121,31 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(smla, "_lib", None)
     with pytest.raises(RuntimeError, match="HIP library missing"):
         smla.lib()
+
+
+@needs_lib
+def test_row_formats_and_stride_limits():
+    # a sequence's rows must stay below 2^31 bytes: the largest stride per format
+    for fmt, rb in ((0, 640), (1, 584)):
+        top = (2 ** 31 - 1) // rb
+        assert smla.num_splits(1, 16, 64, kv_seq_stride=top, row_format=fmt) >= 1
+        assert smla.num_splits(1, 16, 64, kv_seq_stride=top + 1, row_format=fmt) == -1
+    assert smla.num_splits(1, 16, 64, row_format=2) == -1
+    assert smla.workspace_bytes(4, 16, 512, 4, row_format=1) == smla.workspace_bytes(4, 16, 512, 4)
+
+
+def test_shape_struct_matches_header(tmp_path):
+    # the ctypes mirror of smla_shape has the C struct's size and field offsets
+    src = tmp_path / "probe.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "smla.h"\n'
+        'int main(void) { printf("%zu %zu %zu %zu\\n", sizeof(smla_shape), '
+        'offsetof(smla_shape, num_splits), offsetof(smla_shape, kv_seq_stride), '
+        'offsetof(smla_shape, row_format)); return 0; }\n')
+    exe = tmp_path / "probe"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    S = smla.SmlaShape
+    assert [int(x) for x in got] == [ctypes.sizeof(S), S.num_splits.offset, S.kv_seq_stride.offset,
+                                     S.row_format.offset]

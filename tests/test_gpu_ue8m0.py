@@ -1,0 +1,154 @@
+"""GPU parity for the UE8M0 row format (584-byte rows, exponent-byte group
+scales): libsmla.so through its C ABI against the fp64 CPU oracle on the same
+seeded inputs.  Marked ``gpu``."""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mla_decode_02_amd as smla
+from tests._gpu import compare, device_inputs, log, run_decode
+from workloads import ROW_FMT_UE8M0, build_host_cache, config_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_ref(w):
+    cache = build_host_cache(w)
+    out, lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads,
+                                    w.scale, row_format=w.row_format)
+    return out, lse
+
+
+@functools.lru_cache(maxsize=1)
+def cfg_case(n):
+    log(f"building workload config {n} (UE8M0 rows)")
+    w = config_workload(n, row_format=ROW_FMT_UE8M0)
+    out, lse = oracle_ref(w)
+    return w, out, lse
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    cfg_case.cache_clear()
+
+
+@pytest.mark.parametrize("cfg,nsplit", [(1, 1), (1, 2), (2, 0), (3, 0), (3, 1), (3, 4), (4, 0), (5, 0)])
+def test_ue8m0_config_parity(cfg, nsplit):
+    log(f"case: UE8M0 config {cfg} num_splits {nsplit}")
+    w, ref_out, ref_lse = cfg_case(cfg)
+    assert w.row_bytes == 584
+    out, lse = run_decode(w, num_splits=nsplit)
+    compare(out, lse, ref_out, ref_lse, label=f"ue8m0 cfg{cfg}/ns{nsplit}")
+
+
+@pytest.mark.parametrize("heads", [16, 64, 128])
+@pytest.mark.parametrize("topk,nsplit", [(45, 1), (45, 2), (100, 0), (1, 1)])
+def test_ue8m0_head_counts_and_ragged_lists(heads, topk, nsplit):
+    log(f"case: UE8M0 heads {heads} topk {topk} nsplit {nsplit}")
+    w = make_workload(seed=200 + heads + topk, batch=3, heads=heads, topk=topk, seqlens=[300, 50, 7],
+                      kv_seq_stride=300, structure="ragged", q_mult=2.0, row_format=ROW_FMT_UE8M0)
+    ref_out, ref_lse = oracle_ref(w)
+    out, lse = run_decode(w, num_splits=nsplit)
+    compare(out, lse, ref_out, ref_lse, label=f"ue8m0 H{heads}/k{topk}/ns{nsplit}")
+
+
+def test_ue8m0_masked_entries():
+    w = make_workload(seed=207, batch=4, heads=64, topk=128, seqlen=1000, row_format=ROW_FMT_UE8M0)
+    rng = np.random.default_rng(207)
+    w.idx[rng.random(w.idx.shape) < 0.3] = -1
+    w.idx[rng.random(w.idx.shape) < 0.05] = 1000 + 5
+    w.idx[1, :] = -1
+    ref_out, ref_lse = oracle_ref(w)
+    for ns in (1, 3):
+        out, lse = run_decode(w, num_splits=ns)
+        compare(out, lse, ref_out, ref_lse, label=f"ue8m0 masked/ns{ns}")
+        assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+NON_NAN_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+# per-batch group exponent bytes: wide spread, the two ends of the supported
+# range (0 is the subnormal 2^-127; 134 is 2^7), constant, descending
+EXPONENTS = np.array([[103, 110, 117, 124, 127, 130, 134],
+                      [127] * 7,
+                      [0, 1, 2, 126, 128, 133, 134],
+                      [134, 133, 132, 131, 130, 129, 128]], dtype=np.uint8)
+
+
+# scales from 2^-24 up: the value product's fp16 weight 1 * scale is then
+# exact (smaller scales are fp16-flushed there; their outputs are below 2^-15)
+EXACT_EXPONENTS = np.array([[103, 110, 117, 124, 127, 130, 134],
+                            [127] * 7,
+                            [103, 104, 105, 126, 128, 133, 134],
+                            [134, 133, 132, 131, 130, 129, 128]], dtype=np.uint8)
+
+
+def test_ue8m0_single_row_is_reproduced_exactly():
+    # one kept row, q = 0: out is the row itself; every code times a power of
+    # two is a bf16 number, so the result must be exact
+    w = make_workload(seed=208, batch=4, heads=16, topk=8, seqlen=4, row_format=ROW_FMT_UE8M0)
+    for b in range(4):
+        row = w.rows[b, 0].copy()
+        row[:448] = np.resize(np.roll(NON_NAN_CODES, 37 * b), 448)
+        row[448:455] = EXACT_EXPONENTS[b]
+        w.rows[b, :] = row
+    w.idx[:] = -1
+    w.idx[:, 3] = 2
+    w.q_bits[:] = 0
+    ref_out, ref_lse = oracle_ref(w)
+    for ns in (1, 0):
+        out, lse = run_decode(w, num_splits=ns)
+        assert np.array_equal(out, ref_out), ns
+        assert np.all(lse == 0.0)
+
+
+def test_ue8m0_scale_bytes_in_logits():
+    # q = e_i selects one nope column of the one kept row: lse = scale * value_i
+    # with value_i = e4m3(code_i) * 2^(e_(i/64) - 127)
+    w = make_workload(seed=209, batch=16, heads=16, topk=1, seqlen=1, row_format=ROW_FMT_UE8M0)
+    cols = np.arange(256).reshape(16, 16) * 7 % 448
+    for b in range(16):
+        row = w.rows[b, 0].copy()
+        row[:448] = np.resize(np.roll(NON_NAN_CODES, 11 * b), 448)
+        row[448:455] = EXPONENTS[b % 4]
+        w.rows[b, 0] = row
+    w.idx[:] = 0
+    q = np.zeros((16, 16, 512), dtype=np.uint16)
+    for b in range(16):
+        for h in range(16):
+            q[b, h, cols[b, h]] = 0x3F80     # bf16 1.0
+    w.q_bits = q
+    out, lse = run_decode(w, num_splits=1)
+    expect = np.array([[w.scale * oracle.e4m3fn_value(w.rows[b, 0, cols[b, h]])
+                        * oracle.ue8m0_value(w.rows[b, 0, 448 + cols[b, h] // 64])
+                        for h in range(16)] for b in range(16)])
+    assert np.allclose(lse, expect, rtol=1e-6, atol=1e-30)
+
+
+def test_ue8m0_partials_match_oracle_splits():
+    w = make_workload(seed=210, batch=4, heads=64, topk=200, seqlens=[3000, 150, 20, 3000],
+                      kv_seq_stride=3000, structure="ragged", q_mult=4.0, row_format=ROW_FMT_UE8M0)
+    S = smla.num_splits(w.batch, w.heads, w.topk, 3, w.kv_seq_stride, w.row_format)
+    C = smla.split_size(w.batch, w.heads, w.topk, 3, w.kv_seq_stride, w.row_format)
+    cache = build_host_cache(w)
+    ref_o, ref_l = oracle.decode_splits(w, S, cache, chunk=C)
+    q, cache_d, idx, seqlens = device_inputs(w)
+    o = torch.full((4, 64, S, 512), float("nan"), device="cuda:0")
+    l = torch.full((4, 64, S), float("nan"), device="cuda:0")
+    smla.sparse_mla_decode_partials(q, cache_d, idx, seqlens, w.scale, o, l, num_splits=3,
+                                    row_format=w.row_format)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy().astype(np.float64)
+    l = l.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all()
+    assert np.array_equal(np.isneginf(l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.abs(l[fin] - ref_l[fin]).max() <= 1e-3
+    assert np.abs(o - ref_o).max() <= 1e-2 * max(1.0, np.abs(ref_o).max() / 4)
+    assert np.linalg.norm(o - ref_o) / np.linalg.norm(ref_o) <= 5e-3
