@@ -54,6 +54,9 @@ def lib():
         L.oracle_decode.restype = i32
         L.oracle_decode_fmt.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, f64, vp, vp, i32, i32]
         L.oracle_decode_fmt.restype = i32
+        L.oracle_decode_paged.argtypes = [vp, vp, i64, i32, vp, i64, vp, i64, vp, i32, i32, i32, f64, vp,
+                                          vp, i32, i32]
+        L.oracle_decode_paged.restype = i32
         L.oracle_decode_padded512.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, f64, vp, vp]
         L.oracle_decode_padded512.restype = i32
         _lib = L
@@ -117,6 +120,40 @@ def decode_raw(q_bits, cache, kv_seq_stride, idx, seqlens, heads, scale, *, padd
                                        int(row_format))
     del idx_view
     return out, lse, used
+
+
+def decode_paged_raw(q_bits, pool, num_pages, page_size, block_table, idx, seqlens, heads, scale, *,
+                     row_format=0, nthreads=0, idx_offset=0, idx_cols=None):
+    """Oracle over a paged pool: ``pool`` uint8 [num_pages * page_size, row bytes],
+    ``block_table`` int32 [B, pages_per_seq].  Returns out, lse, threads used."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    seqlens = np.ascontiguousarray(seqlens, dtype=np.int32)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    B = q_bits.shape[0]
+    topk = idx.shape[1]
+    if idx_cols is None:
+        idx_cols = topk - idx_offset
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous
+    assert pool.size >= num_pages * page_size * ROW_BYTES_OF_FORMAT[row_format]
+    assert block_table.shape[0] == B
+    out = np.zeros((B, heads, 512), dtype=np.float64)
+    lse = np.zeros((B, heads), dtype=np.float64)
+    ptr = ctypes.c_void_p(idx.ctypes.data + 4 * idx_offset)
+    used = lib().oracle_decode_paged(_p(q_bits), _p(pool), int(num_pages), int(page_size), _p(block_table),
+                                     int(block_table.shape[1]), ptr, topk, _p(seqlens), B, heads, idx_cols,
+                                     float(scale), _p(out), _p(lse), int(nthreads), int(row_format))
+    return out, lse, used
+
+
+def decode_paged(w, layout, pool=None, **kw):
+    """Oracle on a ``workloads.Workload`` stored in the paged ``layout``."""
+    if pool is None:
+        from workloads import build_host_pool
+        pool = build_host_pool(w, layout)
+    out, lse, _ = decode_paged_raw(w.q_bits, pool, layout.num_pages, layout.page_size, layout.block_table,
+                                   w.idx, w.seqlens, w.heads, w.scale, row_format=w.row_format, **kw)
+    return out, lse
 
 
 def decode(w, cache=None, **kw):

@@ -39,6 +39,13 @@ def q_values(q_bits: np.ndarray) -> np.ndarray:
         .view(torch.bfloat16).to(torch.float64).numpy()
 
 
+def _attend(q_b, K, scale):
+    z = scale * (q_b @ K.T)                    # [H,n]
+    l = logsumexp(z, axis=1)
+    p = np.exp(z - l[:, None])
+    return p @ K, l
+
+
 def brute_decode(q_bits, cache, kv_seq_stride, idx, seqlens, scale, row_format=0):
     """Dense fp64 attention restricted to the selected rows (tiny inputs)."""
     q = q_values(q_bits)                       # [B,H,512]
@@ -51,9 +58,30 @@ def brute_decode(q_bits, cache, kv_seq_stride, idx, seqlens, scale, row_format=0
         if not sel:
             continue
         K = dequant_rows_torch(cache[b, sel], row_format)  # [n,512]
-        z = scale * (q[b] @ K.T)               # [H,n]
-        l = logsumexp(z, axis=1)
-        p = np.exp(z - l[:, None])
-        out[b] = p @ K
-        lse[b] = l
+        out[b], lse[b] = _attend(q[b], K, scale)
+    return out, lse
+
+
+def brute_decode_paged(q_bits, pool, num_pages, page_size, block_table, idx, seqlens, scale,
+                       row_format=0):
+    """Dense fp64 attention over a paged pool (tiny inputs): the rows of the
+    kept entries are found with one vectorised block-table lookup
+    (page = table[b, t // page_size], row = page * page_size + t % page_size)."""
+    q = q_values(q_bits)
+    B, H, _ = q.shape
+    rows = pool.reshape(num_pages * page_size, 584 if row_format == 1 else 640)
+    idx = np.asarray(idx, dtype=np.int64)
+    pps = block_table.shape[1]
+    logical_page = np.where(idx >= 0, idx, 0) // page_size
+    in_table = logical_page < pps
+    page = np.take_along_axis(block_table.astype(np.int64), np.minimum(logical_page, pps - 1), axis=1)
+    keep = (idx >= 0) & (idx < np.asarray(seqlens)[:, None]) & in_table & (page >= 0) & (page < num_pages)
+    phys = page * page_size + np.where(idx >= 0, idx, 0) % page_size
+    out = np.zeros((B, H, 512))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        if not keep[b].any():
+            continue
+        K = dequant_rows_torch(rows[phys[b][keep[b]]], row_format)
+        out[b], lse[b] = _attend(q[b], K, scale)
     return out, lse

@@ -14,7 +14,9 @@
  * the 512-wide latent vector: 448 "nope" columns stored as fp8 e4m3fn codes,
  * each 64-column group carrying one scale, and 64 "rope" columns stored as
  * bf16.  Keys and values are the same dequantised latent row.  The oracle
- *   1. keeps the list entries j with 0 <= idx[b,j] < seqlens[b], in list order;
+ *   1. keeps the list entries j with 0 <= idx[b,j] < seqlens[b], in list order
+ *      (with a paged cache also requiring that the entry's page exists, see
+ *      cache_layout below);
  *   2. dequantises each selected row in fp64: K[i] = e4m3(code[i]) * s[i/64]
  *      for i < 448 and K[448+k] = rope[k];
  *   3. z_j = scale * sum_{d<512} q[d] * K_j[d], summed in index order;
@@ -107,18 +109,39 @@ void oracle_dequant_row_fmt(const uint8_t* row, int fmt, double* K) {
 void oracle_dequant_row(const uint8_t* row, double* K) { oracle_dequant_row_fmt(row, 0, K); }
 
 /*
- * q:        bf16 bits [B][H][512]
- * kv:       cache bytes [B][kv_seq_stride][640]
- * idx:      int32, entry (b, j) at idx[b * idx_row_stride + j], j < topk
- * seqlens:  int32 [B]
- * out:      fp64 [B][H][512];  lse: fp64 [B][H]
- * nthreads: OpenMP threads (<= 0: library default).  Returns the thread count used.
+ * Where the cache row of list entry t of sequence b lives.  Contiguous: row t
+ * of sequence b at (b * kv_seq_stride + t) rows from the start.  Paged: the
+ * pool holds pages of page_size rows; block_table[b * pages_per_seq + p] is the
+ * pool page holding positions p * page_size .. (p + 1) * page_size - 1 of
+ * sequence b.  The paged reading of the pages' "paged FP8 format" ("The
+ * Power-of-Two Trap", section "Input Knowledge Required"), which gives no
+ * block size or table: the usual block-table page pool.
  */
-int oracle_decode_fmt(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
-                      const int32_t* idx, int64_t idx_row_stride, const int32_t* seqlens,
-                      int B, int H, int topk, double scale, double* out, double* lse,
-                      int nthreads, int fmt) {
-    const int64_t row_stride = oracle_row_stride(fmt);
+typedef struct {
+    const uint8_t* base;
+    int64_t row_stride;       /* bytes per row */
+    int64_t kv_seq_stride;    /* contiguous: rows per sequence */
+    const int32_t* block_table;   /* NULL: contiguous */
+    int64_t pages_per_seq, num_pages;
+    int32_t page_size;
+} cache_layout;
+
+/* Row of entry t of sequence b, or NULL when the entry is skipped: t < 0,
+ * t >= seqlen, and (paged) a position past the sequence's block-table row or
+ * a page id outside the pool. */
+static const uint8_t* row_of(const cache_layout* c, int b, int32_t t, int32_t seqlen) {
+    if (t < 0 || t >= seqlen) return NULL;
+    if (!c->block_table) return c->base + ((int64_t)b * c->kv_seq_stride + t) * c->row_stride;
+    int64_t p = t / c->page_size;
+    if (p >= c->pages_per_seq) return NULL;
+    int64_t page = c->block_table[(int64_t)b * c->pages_per_seq + p];
+    if (page < 0 || page >= c->num_pages) return NULL;
+    return c->base + (page * c->page_size + t % c->page_size) * c->row_stride;
+}
+
+static int decode_core(const uint16_t* q, const cache_layout* c, const int32_t* idx,
+                       int64_t idx_row_stride, const int32_t* seqlens, int B, int H, int topk,
+                       double scale, double* out, double* lse, int nthreads, int fmt) {
     int used = 1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -140,9 +163,9 @@ int oracle_decode_fmt(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_strid
         double M = -INFINITY;
         int nsel = 0;
         for (int j = 0; j < topk; j++) {
-            int32_t t = idx[(int64_t)b * idx_row_stride + j];
-            if (t < 0 || t >= seqlens[b]) continue;
-            oracle_dequant_row_fmt(kv + ((int64_t)b * kv_seq_stride + t) * row_stride, fmt, K);
+            const uint8_t* row = row_of(c, b, idx[(int64_t)b * idx_row_stride + j], seqlens[b]);
+            if (!row) continue;
+            oracle_dequant_row_fmt(row, fmt, K);
             double z = 0.0;
             for (int d = 0; d < OR_LATENT; d++) z += qd[d] * K[d];
             z *= scale;
@@ -158,9 +181,9 @@ int oracle_decode_fmt(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_strid
         /* pass 2: exact softmax weights and the weighted sum of value rows */
         double L = 0.0;
         for (int j = 0; j < topk; j++) {
-            int32_t t = idx[(int64_t)b * idx_row_stride + j];
-            if (t < 0 || t >= seqlens[b]) continue;
-            oracle_dequant_row_fmt(kv + ((int64_t)b * kv_seq_stride + t) * row_stride, fmt, K);
+            const uint8_t* row = row_of(c, b, idx[(int64_t)b * idx_row_stride + j], seqlens[b]);
+            if (!row) continue;
+            oracle_dequant_row_fmt(row, fmt, K);
             double z = 0.0;
             for (int d = 0; d < OR_LATENT; d++) z += qd[d] * K[d];
             z *= scale;
@@ -172,6 +195,34 @@ int oracle_decode_fmt(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_strid
         lse[bh] = M + log(L);
     }
     return used;
+}
+
+/*
+ * q:        bf16 bits [B][H][512]
+ * kv:       cache bytes [B][kv_seq_stride][row bytes of the format]
+ * idx:      int32, entry (b, j) at idx[b * idx_row_stride + j], j < topk
+ * seqlens:  int32 [B]
+ * out:      fp64 [B][H][512];  lse: fp64 [B][H]
+ * nthreads: OpenMP threads (<= 0: library default).  Returns the thread count used.
+ */
+int oracle_decode_fmt(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,
+                      const int32_t* idx, int64_t idx_row_stride, const int32_t* seqlens,
+                      int B, int H, int topk, double scale, double* out, double* lse,
+                      int nthreads, int fmt) {
+    cache_layout c = {kv, oracle_row_stride(fmt), kv_seq_stride, NULL, 0, 0, 1};
+    return decode_core(q, &c, idx, idx_row_stride, seqlens, B, H, topk, scale, out, lse, nthreads, fmt);
+}
+
+/*
+ * The same step over a paged pool: pool holds num_pages * page_size rows of
+ * the format; block_table int32 [B][pages_per_seq] (see cache_layout).
+ */
+int oracle_decode_paged(const uint16_t* q, const uint8_t* pool, int64_t num_pages, int32_t page_size,
+                        const int32_t* block_table, int64_t pages_per_seq, const int32_t* idx,
+                        int64_t idx_row_stride, const int32_t* seqlens, int B, int H, int topk,
+                        double scale, double* out, double* lse, int nthreads, int fmt) {
+    cache_layout c = {pool, oracle_row_stride(fmt), 0, block_table, pages_per_seq, num_pages, page_size};
+    return decode_core(q, &c, idx, idx_row_stride, seqlens, B, H, topk, scale, out, lse, nthreads, fmt);
 }
 
 int oracle_decode(const uint16_t* q, const uint8_t* kv, int64_t kv_seq_stride,

@@ -291,3 +291,83 @@ def test_ue8m0_dequant_row_matches_brute():
     K = dequant_rows_torch(rows, row_format=1)
     for i in range(rows.shape[0]):
         assert np.array_equal(oracle.dequant_row(rows[i], row_format=1), K[i])
+
+
+# ---------------------------------------------------------------------------
+# Paged cache: rows in a shuffled pool of pages, found through a block table
+# ---------------------------------------------------------------------------
+
+from oracle.brute import brute_decode_paged  # noqa: E402
+from workloads import build_host_pool, make_paged_layout  # noqa: E402
+
+PAGED = [
+    (dict(seed=41, batch=3, heads=16, topk=40, seqlens=[100, 7, 300], structure="ragged",
+          kv_seq_stride=300), 16),
+    (dict(seed=42, batch=2, heads=32, topk=64, seqlen=512, q_mult=4.0), 1),
+    (dict(seed=43, batch=2, heads=16, topk=64, seqlen=500), 64),
+    (dict(seed=44, batch=2, heads=16, topk=32, seqlen=100), 256),
+]
+
+
+@pytest.mark.parametrize("row_format", [0, 1])
+@pytest.mark.parametrize("cfg,page_size", PAGED)
+def test_paged_oracle_matches_brute_force(cfg, page_size, row_format):
+    w = make_workload(row_format=row_format, **cfg)
+    lay = make_paged_layout(w, page_size, seed=cfg["seed"], spare_pages=3)
+    pool = build_host_pool(w, lay)
+    out, lse = oracle.decode_paged(w, lay, pool)
+    bout, blse = brute_decode_paged(w.q_bits, pool, lay.num_pages, page_size, lay.block_table, w.idx,
+                                    w.seqlens, w.scale, row_format)
+    assert np.abs(out - bout).max() <= 1e-12 * max(1.0, np.abs(bout).max())
+    fin = np.isfinite(blse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.abs(lse[fin] - blse[fin]).max() <= 1e-12 * max(1.0, np.abs(blse[fin]).max())
+
+
+@pytest.mark.parametrize("cfg,page_size", PAGED)
+def test_paged_equals_contiguous_bitwise(cfg, page_size):
+    # the same rows reached through a block table give identical bits
+    w = make_workload(**cfg)
+    out, lse, _ = run(w)
+    lay = make_paged_layout(w, page_size, seed=cfg["seed"] + 1, spare_pages=2, all_pages=True)
+    pout, plse = oracle.decode_paged(w, lay)
+    assert np.array_equal(out.view(np.uint64), pout.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), plse.view(np.uint64))
+
+
+def test_paged_page_renaming_is_invariant():
+    w = make_workload(seed=45, batch=3, heads=16, topk=48, seqlen=400)
+    lay = make_paged_layout(w, 32, seed=1, spare_pages=4)
+    pool = build_host_pool(w, lay)
+    out, lse = oracle.decode_paged(w, lay, pool)
+    perm = np.random.default_rng(2).permutation(lay.num_pages)
+    pool2 = np.empty_like(pool).reshape(lay.num_pages, 32, -1)
+    pool2[perm] = pool.reshape(lay.num_pages, 32, -1)
+    bt2 = np.where(lay.block_table >= 0, perm[np.maximum(lay.block_table, 0)], -1).astype(np.int32)
+    out2, lse2, _ = oracle.decode_paged_raw(w.q_bits, pool2.reshape(pool.shape), lay.num_pages, 32, bt2,
+                                            w.idx, w.seqlens, w.heads, w.scale)
+    assert np.array_equal(out.view(np.uint64), out2.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), lse2.view(np.uint64))
+
+
+def test_paged_missing_pages_skip_their_entries():
+    # a block-table slot that is -1, negative or past the pool, and a position
+    # past the table row, each skip the entry: same bits as -1 in the list
+    w = make_workload(seed=46, batch=2, heads=16, topk=64, seqlen=512)
+    lay = make_paged_layout(w, 16, seed=3, spare_pages=2, all_pages=True)
+    pool = build_host_pool(w, lay)
+    bt = lay.block_table.copy()
+    bt[0, 3], bt[0, 7], bt[1, 5] = -1, -9, lay.num_pages + 4
+    short = bt[:, :30]                      # positions >= 480 fall past the table row
+    idx2 = w.idx.copy()
+    lp = np.where(w.idx >= 0, w.idx, 0) // 16
+    drop = ((np.arange(2)[:, None] == 0) & ((lp == 3) | (lp == 7))) | \
+           ((np.arange(2)[:, None] == 1) & (lp == 5)) | (lp >= 30)
+    assert drop.sum() > 0
+    idx2[drop] = -1
+    out, lse, _ = oracle.decode_paged_raw(w.q_bits, pool, lay.num_pages, 16, short, w.idx, w.seqlens,
+                                          w.heads, w.scale)
+    ref, rlse, _ = oracle.decode_paged_raw(w.q_bits, pool, lay.num_pages, 16, lay.block_table, idx2,
+                                           w.seqlens, w.heads, w.scale)
+    assert np.array_equal(out.view(np.uint64), ref.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), rlse.view(np.uint64))

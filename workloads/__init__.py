@@ -16,12 +16,16 @@ from .generate import (  # noqa: F401
     ROW_BYTES_OF_FORMAT,
     ROW_FMT_FP32,
     ROW_FMT_UE8M0,
+    PagedLayout,
     Workload,
     bf16_bits_from_f32,
     build_host_cache,
+    build_host_pool,
     config_workload,
     encode_e4m3fn,
+    make_paged_layout,
     make_workload,
+    physical_rows,
     quantise_rows,
     ue8m0_exponents,
 )

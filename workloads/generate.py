@@ -264,3 +264,61 @@ def build_host_cache(w: Workload) -> np.ndarray:
     b_i, j_i = np.nonzero(v)
     cache[b_i, w.idx[b_i, j_i]] = w.rows[b_i, j_i]
     return cache
+
+
+# --------------------------------------------------------------------------
+# paged cache layout (input placement only)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PagedLayout:
+    """Rows of every sequence in one pool of pages of ``page_size`` rows:
+    ``block_table[b, p]`` is the pool page that holds positions
+    p*page_size .. (p+1)*page_size - 1 of sequence b (-1: not allocated)."""
+    page_size: int
+    num_pages: int
+    block_table: np.ndarray   # int32 [B, pages_per_seq]
+
+    @property
+    def pages_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def make_paged_layout(w: Workload, page_size: int, *, seed: int = 0, spare_pages: int = 0,
+                      all_pages: bool = False) -> PagedLayout:
+    """Place the workload's rows in a shuffled pool.  A logical page gets a pool
+    page when a kept list entry falls in it (every page below the sequence
+    length with ``all_pages``); the others stay -1.  Pool pages are a random
+    permutation (seeded), plus ``spare_pages`` pages that no sequence uses."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    pps = max(1, -(-int(w.seqlens.max() if w.batch else 1) // page_size))
+    need = np.zeros((w.batch, pps), dtype=bool)
+    if all_pages:
+        for b in range(w.batch):
+            need[b, : -(-int(w.seqlens[b]) // page_size)] = True
+    b_i, j_i = np.nonzero(w.valid)
+    need[b_i, w.idx[b_i, j_i] // page_size] = True
+    n_used = int(need.sum())
+    num_pages = n_used + spare_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((w.batch, pps), -1, dtype=np.int32)
+    bt[need] = perm[:n_used]
+    return PagedLayout(page_size=int(page_size), num_pages=int(num_pages), block_table=bt)
+
+
+def physical_rows(w: Workload, layout: PagedLayout) -> np.ndarray:
+    """Pool row of every list entry (-1 for an entry that is not kept)."""
+    ps = layout.page_size
+    t = np.where(w.valid, w.idx, 0).astype(np.int64)
+    b = np.arange(w.batch)[:, None]
+    page = layout.block_table[b, t // ps].astype(np.int64)
+    return np.where(w.valid, page * ps + t % ps, -1)
+
+
+def build_host_pool(w: Workload, layout: PagedLayout) -> np.ndarray:
+    """The pool uint8 [num_pages * page_size, row bytes]: kept rows placed, rest 0xFF."""
+    pool = np.full((layout.num_pages * layout.page_size, w.row_bytes), 0xFF, dtype=np.uint8)
+    phys = physical_rows(w, layout)
+    b_i, j_i = np.nonzero(w.valid)
+    pool[phys[b_i, j_i]] = w.rows[b_i, j_i]
+    return pool
