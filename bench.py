@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=3, help="workload number 1..5 (default 3)")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="0 = contiguous cache; else rows in a shuffled paged pool of this page size")
     ap.add_argument("--row-format", type=int, default=0, choices=(0, 1),
                     help="cache rows: 0 = fp32 group scales (640 B), 1 = UE8M0 scale bytes (584 B)")
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto, > 768 MB)")
@@ -100,7 +102,7 @@ def main():
     import torch
 
     import sparse_mla_decode_02_amd as smla
-    from workloads import config_workload
+    from workloads import config_workload, make_paged_layout, physical_rows
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -121,10 +123,18 @@ def main():
 
     # ---- device inputs: R rotating copies
     b_i, j_i = np.nonzero(valid)
-    flat = torch.from_numpy(b_i.astype(np.int64) * w.kv_seq_stride + w.idx[b_i, j_i]).to(dev)
+    paged = args.page_size > 0
+    if paged:
+        lay = make_paged_layout(w, args.page_size, seed=args.config, spare_pages=64)
+        flat = torch.from_numpy(physical_rows(w, lay)[b_i, j_i]).to(dev)
+        cache_rows = lay.num_pages * lay.page_size
+        log(f"paged pool: page size {lay.page_size}, {lay.num_pages} pages, table {lay.block_table.shape}")
+    else:
+        flat = torch.from_numpy(b_i.astype(np.int64) * w.kv_seq_stride + w.idx[b_i, j_i]).to(dev)
+        cache_rows = B * w.kv_seq_stride
     rows = torch.from_numpy(np.ascontiguousarray(w.rows[b_i, j_i])).to(dev)
     step_bytes = n_rows * RB + B * H * 512 * 2 * 2 + B * K * 4
-    cache_bytes = B * w.kv_seq_stride * RB
+    cache_bytes = cache_rows * RB
     if args.warm:
         R = 1
     elif args.rotate > 0:
@@ -136,10 +146,11 @@ def main():
     q0 = torch.from_numpy(w.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     idx0 = torch.from_numpy(w.idx).to(dev)
     sl0 = torch.from_numpy(w.seqlens).to(dev)
+    bt0 = torch.from_numpy(lay.block_table).to(dev) if paged else None
     for r in range(R):
-        cache = torch.full((B, w.kv_seq_stride, RB), 0xFF, dtype=torch.uint8, device=dev)
-        cache.view(-1, RB)[flat] = rows
-        sets.append((q0.clone(), cache, idx0.clone(), sl0.clone()))
+        cache = torch.full((cache_rows, RB), 0xFF, dtype=torch.uint8, device=dev)
+        cache[flat] = rows
+        sets.append((q0.clone(), cache, idx0.clone(), sl0.clone(), bt0.clone() if paged else None))
     out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     o_part = torch.empty((B, H, ns, 512), dtype=torch.float32, device=dev)
@@ -153,6 +164,7 @@ def main():
     import ctypes
     L = smla.lib()
     shape = smla.make_shape(B, H, K, args.num_splits, w.kv_seq_stride, fmt)
+    pg = smla.make_paged(lay.page_size, lay.pages_per_seq, lay.num_pages) if paged else None
     hs = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     dec_args, full_args = [], []
@@ -160,24 +172,32 @@ def main():
     need_ws = smla.workspace_bytes(B, H, K, args.num_splits, w.kv_seq_stride, fmt)
     if need_ws:
         ws = torch.empty(need_ws, dtype=torch.uint8, device=dev)
-    for q, cache, idx, sl in sets:
-        dec_args.append((P(q), P(cache), P(idx), P(sl), ctypes.c_float(w.scale), ctypes.byref(shape),
-                         P(o_part), P(lse_part), hs))
-        full_args.append((P(q), P(cache), P(idx), P(sl), ctypes.c_float(w.scale), P(out), P(lse),
-                          ctypes.byref(shape), P(ws) if ws is not None else None, ctypes.c_size_t(need_ws), hs))
-    comb_args = (P(o_part), P(lse_part), B, H, ns, P(out), P(lse), hs)
+    wsp = P(ws) if ws is not None else None
+    for q, cache, idx, sl, bt in sets:
+        if paged:
+            dec_args.append((P(q), P(cache), P(bt), P(idx), P(sl), ctypes.c_float(w.scale), ctypes.byref(shape),
+                             ctypes.byref(pg), P(o_part), P(lse_part), hs))
+            full_args.append((P(q), P(cache), P(bt), P(idx), P(sl), ctypes.c_float(w.scale), P(out), P(lse),
+                              ctypes.byref(shape), ctypes.byref(pg), wsp, ctypes.c_size_t(need_ws), hs))
+        else:
+            dec_args.append((P(q), P(cache), P(idx), P(sl), ctypes.c_float(w.scale), ctypes.byref(shape),
+                             P(o_part), P(lse_part), hs))
+            full_args.append((P(q), P(cache), P(idx), P(sl), ctypes.c_float(w.scale), P(out), P(lse),
+                              ctypes.byref(shape), wsp, ctypes.c_size_t(need_ws), hs))
+    decode_fn = L.sparse_mla_decode_paged if paged else L.sparse_mla_decode
+    partials_fn = L.sparse_mla_decode_partials_paged if paged else L.sparse_mla_decode_partials
 
     def step(i):
         """One whole step: decode kernel, then the combine kernel when split."""
-        st = L.sparse_mla_decode(*full_args[i % R])
+        st = decode_fn(*full_args[i % R])
         assert st == 0, st
 
     def decode_only(i):
         """The decode kernel alone (split partials when the list is split)."""
         if ns == 1:
-            st = L.sparse_mla_decode(*full_args[i % R])
+            st = decode_fn(*full_args[i % R])
         else:
-            st = L.sparse_mla_decode_partials(*dec_args[i % R])
+            st = partials_fn(*dec_args[i % R])
         assert st == 0, st
 
     if args.copy_calibration_mib > 0:
@@ -260,9 +280,10 @@ def main():
                    "topk": K, "seq_len": int(w.kv_seq_stride), "kept_rows": n_rows,
                    "num_splits": ns, "split_size": chunk, "rotation": R,
                    "row_format": "ue8m0_scales_584B" if fmt == 1 else "fp32_scales_640B",
+                   "cache": f"paged, {args.page_size} rows per page" if paged else "contiguous per sequence",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": counted_traffic(args.config, fmt)},
+                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": None if paged else counted_traffic(args.config, fmt)},
         "cpu_baseline": cpu,
         "effective_kv_gbps": kv_gbps,
         "all_algorithmic_gbps": all_bytes / t_dec / 1e9,

@@ -153,6 +153,51 @@ smla_status sparse_mla_decode_partials(const void* q, const void* kv_cache,
                                        float scale, const smla_shape* shape, float* o_part,
                                        float* lse_part, void* stream);
 
+/*
+ * Paged cache: the rows of all sequences live in one pool of pages of
+ * page_size rows each (row bytes per shape->row_format), and
+ * block_table[b][p] (int32 [B][pages_per_seq]) is the pool page that holds
+ * positions p * page_size .. (p + 1) * page_size - 1 of sequence b: list entry
+ * t of sequence b is pool row block_table[b][t / page_size] * page_size +
+ * t % page_size.  The pages describe the deployed cache as paged ("The
+ * Power-of-Two Trap", section "Input Knowledge Required") without giving a
+ * block size or table; this is the usual block-table pool.
+ */
+typedef struct {
+    int32_t page_size;      /* rows per page: a power of two, 1 .. 2^20 */
+    int32_t pages_per_seq;  /* 1 .. 2^29: entries per block-table row */
+    int64_t num_pages;      /* >= 1: pages in the pool; num_pages * page_size < 2^32 */
+} smla_paged;
+
+/*
+ * sparse_mla_decode_paged -- sparse_mla_decode over a paged pool.
+ *
+ *   kv_pool     bytes [num_pages * page_size][R], 16-byte aligned (R = row bytes
+ *               of shape->row_format); may exceed 4 GB
+ *   block_table int32 [B][pages_per_seq], 4-byte aligned
+ *   paged       page geometry, see smla_paged
+ *   shape       as for sparse_mla_decode; kv_seq_stride is not used (pass 1)
+ *   all other arguments as for sparse_mla_decode.
+ * A list entry is skipped when it is < 0 or >= seqlens[b] (as before), when
+ * t / page_size >= pages_per_seq, or when its block-table slot is negative or
+ * >= num_pages.  The result is that of sparse_mla_decode on a contiguous
+ * cache holding the same rows.  Invalid page geometry returns SMLA_ERR_SHAPE;
+ * a NULL paged or (topk > 0) block_table returns SMLA_ERR_NULL.
+ */
+smla_status sparse_mla_decode_paged(const void* q, const void* kv_pool, const int32_t* block_table,
+                                    const int32_t* topk_idx, const int32_t* seqlens, float scale,
+                                    void* out, float* lse, const smla_shape* shape,
+                                    const smla_paged* paged, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* The decode kernel of sparse_mla_decode_paged alone: split partials as for
+ * sparse_mla_decode_partials. */
+smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool,
+                                             const int32_t* block_table, const int32_t* topk_idx,
+                                             const int32_t* seqlens, float scale,
+                                             const smla_shape* shape, const smla_paged* paged,
+                                             float* o_part, float* lse_part, void* stream);
+
 /* List entries per split (C above, a multiple of 32); -1 for an invalid shape. */
 int32_t smla_split_size(const smla_shape* shape);
 

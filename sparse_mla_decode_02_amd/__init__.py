@@ -30,6 +30,7 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine",
+           "sparse_mla_decode_paged", "sparse_mla_decode_partials_paged",
            "smla_workspace_bytes", "smla_num_splits", "smla_split_size", "smla_status_str")
 
 
@@ -37,6 +38,11 @@ class SmlaShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("kv_seq_stride", ctypes.c_int64), ("row_format", ctypes.c_int32)]
+
+
+class SmlaPaged(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64)]
 
 
 class SmlaError(RuntimeError):
@@ -71,6 +77,11 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_decode.restype = ctypes.c_int
         L.sparse_mla_combine.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.sparse_mla_combine.restype = ctypes.c_int
+        pgd = ctypes.POINTER(SmlaPaged)
+        L.sparse_mla_decode_paged.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, shp, pgd, vp, ctypes.c_size_t, vp]
+        L.sparse_mla_decode_paged.restype = ctypes.c_int
+        L.sparse_mla_decode_partials_paged.argtypes = [vp, vp, vp, vp, vp, f32, shp, pgd, vp, vp, vp]
+        L.sparse_mla_decode_partials_paged.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -170,3 +181,50 @@ def sparse_mla_combine(o_part, lse_part, out, lse, *, stream=None):
     _check(lib().sparse_mla_combine(_ptr(o_part), _ptr(lse_part), B, H, S, _ptr(out), _ptr(lse),
                                     _stream_handle(stream)))
     return out, lse
+
+
+def make_paged(page_size, pages_per_seq, num_pages) -> SmlaPaged:
+    return SmlaPaged(int(page_size), int(pages_per_seq), int(num_pages))
+
+
+def sparse_mla_decode_paged(q, kv_pool, block_table, topk_idx, seqlens, scale, out, lse, *, page_size,
+                            num_pages=None, num_splits=0, workspace=None, stream=None, row_format=0):
+    """One decode step over a paged pool through libsmla.so.
+
+    kv_pool: uint8 [num_pages * page_size, R] (or flat), R = 640 / 584 for
+    row_format 0 / 1; block_table: int32 [B, pages_per_seq]; the rest as for
+    sparse_mla_decode.
+    """
+    import torch
+    B, H, _ = q.shape
+    topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    if num_pages is None:
+        num_pages = kv_pool.numel() // (ROW_BYTES_OF_FORMAT.get(row_format, ROW_BYTES) * page_size)
+    shape = make_shape(B, H, topk, num_splits, 1, row_format)
+    paged = make_paged(page_size, block_table.shape[1], num_pages)
+    L = lib()
+    need = int(L.smla_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.sparse_mla_decode_paged(_ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(topk_idx), _ptr(seqlens),
+                                     ctypes.c_float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape),
+                                     ctypes.byref(paged), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+                                     _stream_handle(stream)))
+    return out, lse
+
+
+def sparse_mla_decode_partials_paged(q, kv_pool, block_table, topk_idx, seqlens, scale, o_part, lse_part, *,
+                                     page_size, num_pages=None, num_splits=0, stream=None, row_format=0):
+    """Decode kernel only over a paged pool: split partials as sparse_mla_decode_partials."""
+    B, H, _ = q.shape
+    topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    if num_pages is None:
+        num_pages = kv_pool.numel() // (ROW_BYTES_OF_FORMAT.get(row_format, ROW_BYTES) * page_size)
+    shape = make_shape(B, H, topk, num_splits, 1, row_format)
+    paged = make_paged(page_size, block_table.shape[1], num_pages)
+    _check(lib().sparse_mla_decode_partials_paged(_ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(topk_idx),
+                                                  _ptr(seqlens), ctypes.c_float(scale), ctypes.byref(shape),
+                                                  ctypes.byref(paged), _ptr(o_part), _ptr(lse_part),
+                                                  _stream_handle(stream)))
+    return o_part, lse_part

@@ -277,6 +277,33 @@ __device__ __forceinline__ void gather4_at(uint32_t voff, i32x4 rsrc, uint32_t l
                  : "m0");
 }
 
+// The same gathers from 64-bit per-lane addresses (paged pool, which may
+// exceed the 4 GB that a buffer instruction's 32-bit offset reaches):
+// global_load_lds_dword{,x4}; the LDS destination follows the same rule
+// (M0 + instruction offset + 4 or 16 * lane, checked on gfx950).  There is no
+// range check: a masked lane reads the zero row below instead.
+template <int kOff>
+__device__ __forceinline__ void gather16_global_at(const uint8_t* a, uint32_t lds_base) {
+    static_assert(kOff >= 0 && kOff < 4096, "global instruction offset");
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+                 :
+                 : "v"(a), "s"(__builtin_amdgcn_readfirstlane(lds_base - kOff)), "n"(kOff)
+                 : "m0");
+}
+
+template <int kOff>
+__device__ __forceinline__ void gather4_global_at(const uint8_t* a, uint32_t lds_base) {
+    static_assert(kOff >= 0 && kOff < 4096, "global instruction offset");
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off offset:%2"
+                 :
+                 : "v"(a), "s"(__builtin_amdgcn_readfirstlane(lds_base - kOff)), "n"(kOff)
+                 : "m0");
+}
+
+// Source of the masked rows of a paged gather: a row of zeros (finite, adds
+// nothing), as long as the largest row format.
+__device__ __attribute__((aligned(64))) const uint8_t kZeroRow[SMLA_ROW_BYTES] = {0};
+
 template <int K, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (K < N) {
@@ -319,6 +346,11 @@ struct DecodeArgs {
     int32_t force_partials;   // write split partials even when nsplit == 1
     int32_t xcd_remap;        // grid is a multiple of 8: keep a sequence's blocks on one XCD
     int32_t row_format;       // host only: selects the kernel instance
+    // paged pool (kv is the pool): block_table [batch][pages_per_seq]
+    const int32_t* block_table;
+    int32_t page_shift;       // log2 rows per page
+    int32_t pages_per_seq;
+    uint32_t pool_rows;       // num_pages << page_shift (< 2^32)
 };
 
 // Gather one whole 32-token tile into the LDS slot at slot_lds.  Lane l holds
@@ -333,55 +365,79 @@ struct DecodeArgs {
 // group 7 (padding), whose row holds list entries instead (see
 // load_entries_lds).  UE8M0 scales: one gather of 4 bytes per lane (see
 // kScaleRaw).
+// Source addresses: a byte offset from the sequence's first row (contiguous
+// cache, through the buffer resource), or a 64-bit address (paged pool; a
+// masked row reads kZeroRow).
+template <bool P>
 struct TileGather {
-    uint32_t v0, v1;     // source offsets for the blocks of positions 0..15 and 16..31
-    uint32_t vscale;     // source offset of this lane's scale pair
+    using Addr = std::conditional_t<P, const uint8_t*, uint32_t>;
+    Addr v0, v1;         // blocks of positions 0..15 and 16..31
+    Addr vscale;         // this lane's scale pair
     uint32_t slot;       // LDS slot address
 };
 
-template <int F>
-__device__ __forceinline__ TileGather plan_tile(int row, uint32_t slot_lds, int lane) {
+template <int F, bool P>
+__device__ __forceinline__ typename TileGather<P>::Addr source(int row, uint32_t off, const uint8_t* pool) {
+    if constexpr (P)
+        return (row == -1 ? kZeroRow : pool + (uint64_t)(uint32_t)row * RowFormat<F>::kBytes) + off;
+    else return row_offset<F>(row, off);
+}
+
+template <int F, bool P>
+__device__ __forceinline__ TileGather<P> plan_tile(int row, uint32_t slot_lds, int lane, const uint8_t* pool) {
     const int row0 = __builtin_amdgcn_ds_bpermute(4 * (lane >> 2), row);
     const int row1 = __builtin_amdgcn_ds_bpermute(4 * (16 + (lane >> 2)), row);
     const uint32_t pp = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    TileGather g;
-    g.v0 = row_offset<F>(row0, 16u * pp);
-    g.v1 = row_offset<F>(row1, 16u * pp);
-    g.vscale = row_offset<F>(row, SMLA_SCALE_OFFSET + 4u * ((uint32_t)lane >> 5));
+    TileGather<P> g;
+    g.v0 = source<F, P>(row0, 16u * pp, pool);
+    g.v1 = source<F, P>(row1, 16u * pp, pool);
+    g.vscale = source<F, P>(row, SMLA_SCALE_OFFSET + 4u * ((uint32_t)lane >> 5), pool);
     g.slot = slot_lds;
     return g;
 }
 
-template <int F>
-__device__ __forceinline__ void issue_scales(const TileGather& g, i32x4 rsrc, int lane) {
+template <int kOff, bool P>
+__device__ __forceinline__ void gather16(const typename TileGather<P>::Addr& v, i32x4 rsrc, uint32_t lds_base) {
+    if constexpr (P) gather16_global_at<kOff>(v, lds_base);
+    else gather16_at<kOff>(v, rsrc, lds_base);
+}
+
+template <int kOff, bool P>
+__device__ __forceinline__ void gather4s(const typename TileGather<P>::Addr& v, i32x4 rsrc, uint32_t lds_base) {
+    if constexpr (P) gather4_global_at<kOff>(v, lds_base);
+    else gather4_at<kOff>(v, rsrc, lds_base);
+}
+
+template <int F, bool P>
+__device__ __forceinline__ void issue_scales(const TileGather<P>& g, i32x4 rsrc, int lane) {
     if constexpr (F == SMLA_ROW_UE8M0_SCALES) {
-        gather4_at<0>(g.vscale, rsrc, g.slot + kScaleRaw);
+        gather4s<0, P>(g.vscale, rsrc, g.slot + kScaleRaw);
     } else {
         static_for<0, kScaleGathers - 1>([&](auto kc) {
             constexpr int k = decltype(kc)::value;
-            gather4_at<8 * k>(g.vscale, rsrc, g.slot + kScaleTable + 256 * k);
+            gather4s<8 * k, P>(g.vscale, rsrc, g.slot + kScaleTable + 256 * k);
         });
         if (lane < 32)
-            gather4_at<8 * (kScaleGathers - 1)>(g.vscale, rsrc, g.slot + kScaleTable + 256 * (kScaleGathers - 1));
+            gather4s<8 * (kScaleGathers - 1), P>(g.vscale, rsrc, g.slot + kScaleTable + 256 * (kScaleGathers - 1));
     }
 }
 
 // Blocks 2j and 2j + 1 for j in [J0, J1).
-template <int F, int J0, int J1>
-__device__ __forceinline__ void issue_blocks(const TileGather& g, i32x4 rsrc) {
+template <int F, int J0, int J1, bool P>
+__device__ __forceinline__ void issue_blocks(const TileGather<P>& g, i32x4 rsrc) {
     static_for<J0, J1>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int off = 64 * j + (4 * j >= kCodePieces ? RowFormat<F>::kRopeOff - SMLA_SCALE_OFFSET : 0);
-        gather16_at<off>(g.v0, rsrc, g.slot + 1024 * (2 * j));
-        gather16_at<off>(g.v1, rsrc, g.slot + 1024 * (2 * j + 1));
+        gather16<off, P>(g.v0, rsrc, g.slot + 1024 * (2 * j));
+        gather16<off, P>(g.v1, rsrc, g.slot + 1024 * (2 * j + 1));
     });
 }
 
-template <int F>
-__device__ __forceinline__ void issue_tile(int row, i32x4 rsrc, uint32_t slot_lds, int lane) {
-    const TileGather g = plan_tile<F>(row, slot_lds, lane);
-    issue_scales<F>(g, rsrc, lane);
-    issue_blocks<F, 0, kRowGathers / 2>(g, rsrc);
+template <int F, bool P>
+__device__ __forceinline__ void issue_tile(int row, i32x4 rsrc, uint32_t slot_lds, int lane, const uint8_t* pool) {
+    const TileGather<P> g = plan_tile<F, P>(row, slot_lds, lane, pool);
+    issue_scales<F, P>(g, rsrc, lane);
+    issue_blocks<F, 0, kRowGathers / 2, P>(g, rsrc);
 }
 
 // Value 2^(e - 127) of a UE8M0 scale byte as fp32: the exponent field alone,
@@ -659,14 +715,21 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
     combine_row(o_part, lse_part, row, nsplit, out, lse, threadIdx.x & 63);
 }
 
+// Paged pool: the page ids of a tile's entries, 32 per wave and slot, after
+// the tile slots.
+constexpr int kPageIds = kLdsBytes;
+constexpr int kPagedLdsBytes = kLdsBytes + kWaves * 2 * kTile * 4;
+static_assert(kPagedLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+
 // One workgroup = (sequence b, block hb of 16 heads, split).  Its four waves
 // decode the split's tiles independently (wave w takes tiles w, w + 4, ...,
 // each gathered into the wave's own two LDS slots one tile ahead), then merge
 // their online-softmax states once, through LDS, and write the split's
 // normalised output and log-sum-exp (or the final bf16 result).
-template <int F>
+// F: row format; P: rows in a paged pool found through the block table.
+template <int F, bool P>
 __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[P ? kPagedLdsBytes : kLdsBytes];
     lds_u8* const lds = (lds_u8*)lds_raw;
 
     const int lane = threadIdx.x & 63;
@@ -686,7 +749,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
     const int ntiles = (n_ent + kTile - 1) / kTile;
     const int seqlen = a.seqlens[b];
-    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
+    // contiguous cache: a buffer resource over the sequence's rows
+    const i32x4 rsrc = P ? i32x4{0, 0, 0, 0}
+                         : row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
     const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
 
     // ---- the query of this lane's head as the B operand of S^T = K . Q^T
@@ -733,6 +798,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         return first_entry(i) + (lane & 31) < n_ent && v >= 0 && v < seqlen ? v : -1;
     };
     int row_cur = -1, row_1 = -1, row_2 = -1;
+    // Paged pool: a kept entry e of the sequence is at pool row
+    // (block_table[b][e >> page_shift] << page_shift) + (e & (page - 1)).  The
+    // page ids take one more memory round trip, so the pipeline runs one tile
+    // further ahead: the entries of tile i + 3 (into LDS) and the page ids of
+    // tile i + 2 (into LDS, from the entries read at the top of tile i) are
+    // loaded during tile i, and tile i + 1's rows are formed at its top.
+    const int32_t* bt_b = P ? a.block_table + (int64_t)b * a.pages_per_seq : nullptr;
+    const uint32_t page_mask = (1u << a.page_shift) - 1u;
+    // sanitised entry -> pool row, or -1 (no page, or past the table row)
+    auto to_pool_row = [&](int e, int page) -> int {
+        return e >= 0 && (e >> a.page_shift) < a.pages_per_seq && page >= 0 &&
+                       (uint32_t)page < (a.pool_rows >> a.page_shift)
+                   ? (int)(((uint32_t)page << a.page_shift) | ((uint32_t)e & page_mask))
+                   : -1;
+    };
+    auto page_of = [&](int e) -> int { return bt_b[e >= 0 ? min(e >> a.page_shift, a.pages_per_seq - 1) : 0]; };
+    const i32x4 bt_rsrc = P ? row_rsrc((const uint8_t*)bt_b, 4u * (uint32_t)a.pages_per_seq) : i32x4{0, 0, 0, 0};
+    lds_u8* const my_page_ids = lds + kPageIds + wave * 2 * kTile * 4;   // two tiles' page ids
+    const uint32_t my_pages = (uint32_t)(uintptr_t)my_page_ids;
+    int e_n1 = -1, e_n2 = -1;   // sanitised entries of tiles i + 1 and i + 2 (paged)
     if (my_n > 0) {
         const int e0 = load_entry(0);
         const int e1 = load_entry(min(1, my_n - 1));
@@ -740,44 +825,70 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
         row_cur = sanitise(0, e0);
         row_1 = sanitise(1, e1);
         row_2 = sanitise(2, e2);
-        issue_tile<F>(row_cur, rsrc, my_lds_addr, lane);
+        if constexpr (P) {
+            e_n1 = row_1;
+            e_n2 = row_2;
+            const int pg0 = page_of(row_cur), pg1 = page_of(row_1);
+            row_cur = to_pool_row(row_cur, pg0);
+            row_1 = to_pool_row(row_1, pg1);
+        }
+        issue_tile<F, P>(row_cur, rsrc, my_lds_addr, lane, a.kv);
     }
     // the query lands while the first tile is gathered
     load_query();
     pin_state(qop, acc_o);
     for (int i = 0; i < my_n; i++) {
         pin_state(qop, acc_o);
-        wait_vmcnt<0>();   // tile i has landed, and the entries of tile i + 1 (i >= 2)
+        wait_vmcnt<0>();   // tile i has landed, and the entries (and page ids) loaded with it
         const int slot1 = (i + 1) & 1;
-        const int row_next = i == 0   ? row_1
-                             : i == 1 ? row_2
-                                      : sanitise(i + 1, ((lds_ci32*)(my_lds + slot1 * kSlot + kEntryTable))[lane & 31]);
+        int row_next;
+        if constexpr (P) {
+            row_next = i == 0 ? row_1
+                              : to_pool_row(e_n1, ((lds_ci32*)(my_page_ids + slot1 * kTile * 4))[lane & 31]);
+            if (i >= 1 && i + 2 < my_n)
+                e_n2 = sanitise(i + 2, ((lds_ci32*)(my_lds + (i & 1) * kSlot + kEntryTable))[lane & 31]);
+        } else {
+            row_next = i == 0   ? row_1
+                       : i == 1 ? row_2
+                                : sanitise(i + 1, ((lds_ci32*)(my_lds + slot1 * kSlot + kEntryTable))[lane & 31]);
+        }
         // the gathers of tile i + 1: the scales and two blocks now, the rest
         // within the logit product of tile i (early enough for the memory-bound
         // lists); then the entries of tile i + 2, into the slot being computed
         // (its entry table is not read by the compute)
         const bool more = i + 1 < my_n;
-        TileGather tg = {};
+        TileGather<P> tg = {};
         if (more) {
-            tg = plan_tile<F>(row_next, my_lds_addr + slot1 * kSlot, lane);
-            issue_scales<F>(tg, rsrc, lane);
-            issue_blocks<F, 0, 2>(tg, rsrc);
+            tg = plan_tile<F, P>(row_next, my_lds_addr + slot1 * kSlot, lane, a.kv);
+            issue_scales<F, P>(tg, rsrc, lane);
+            issue_blocks<F, 0, 2, P>(tg, rsrc);
         }
         auto issue_part = [&](auto stage) {
             if (!more) return;
             constexpr int k = decltype(stage)::value;
             if constexpr (k == 0) {
-                issue_blocks<F, 2, 6>(tg, rsrc);
+                issue_blocks<F, 2, 6, P>(tg, rsrc);
             } else if constexpr (k == 1) {
-                issue_blocks<F, 6, kRowGathers / 2>(tg, rsrc);
-                if (i >= 1 && i + 2 < my_n)
-                    load_entries_lds(first_entry(i + 2), idx_rsrc, my_lds_addr + (i & 1) * kSlot, lane);
+                issue_blocks<F, 6, kRowGathers / 2, P>(tg, rsrc);
+                if constexpr (P) {
+                    // page ids of tile i + 2 (into page slot i & 1), entries of
+                    // tile i + 3 (into the entry table of slot (i + 1) & 1)
+                    if (i + 2 < my_n && lane < 32)
+                        gather4(e_n2 >= 0 ? 4u * (uint32_t)(e_n2 >> a.page_shift) : 0x80000000u, bt_rsrc,
+                                my_pages + (i & 1) * kTile * 4);
+                    if (i + 3 < my_n)
+                        load_entries_lds(first_entry(i + 3), idx_rsrc, my_lds_addr + slot1 * kSlot, lane);
+                } else {
+                    if (i >= 1 && i + 2 < my_n)
+                        load_entries_lds(first_entry(i + 2), idx_rsrc, my_lds_addr + (i & 1) * kSlot, lane);
+                }
             }
         };
-        const uint64_t vmask = mask_by_token(__ballot(lane < kTile && row_cur >= 0));
+        const uint64_t vmask = mask_by_token(__ballot(lane < kTile && row_cur != -1));
         if constexpr (F == SMLA_ROW_UE8M0_SCALES) expand_ue8m0_scales(my_lds + (i & 1) * kSlot, lane);
         compute_tile(my_lds + (i & 1) * kSlot, vmask, qop, acc_o, m_run, l_run, lane, a.logit_factor, issue_part);
         row_cur = row_next;
+        if constexpr (P) e_n1 = e_n2;
     }
     wait_vmcnt<0>();
 
@@ -854,13 +965,27 @@ int row_bytes_of(int32_t fmt) {
     return fmt == SMLA_ROW_FP32_SCALES ? SMLA_ROW_BYTES : fmt == SMLA_ROW_UE8M0_SCALES ? SMLA_ROW_BYTES_UE8M0 : 0;
 }
 
-// Rows of one sequence are addressed by 32-bit byte offsets below 2^31.
+// Rows of one sequence are addressed by 32-bit byte offsets below 2^31.  (The
+// paged calls do not use the stride but check it the same way.)
 bool shape_ok(const smla_shape* s) {
-    if (!s) return false;
-    const int rb = row_bytes_of(s->row_format);
-    return rb > 0 && s->batch >= 0 && s->num_heads >= 0 && s->num_heads % 16 == 0 &&
-           s->num_heads <= 256 && s->topk >= 0 && s->num_splits >= 0 && s->kv_seq_stride >= 1 &&
-           s->kv_seq_stride <= (((int64_t)1 << 31) - 1) / rb;
+    return s && row_bytes_of(s->row_format) > 0 && s->batch >= 0 && s->num_heads >= 0 &&
+           s->num_heads % 16 == 0 && s->num_heads <= 256 && s->topk >= 0 && s->num_splits >= 0 &&
+           s->kv_seq_stride >= 1 && s->kv_seq_stride <= (((int64_t)1 << 31) - 1) / row_bytes_of(s->row_format);
+}
+
+// Paged pool: rows are record indices below 2^32 - 1 (the all-ones index is the
+// masked row), the block-table row is a raw buffer below 2^31 bytes.
+bool paged_ok(const smla_paged* g) {
+    if (!g || g->page_size < 1 || g->page_size > (1 << 20) || (g->page_size & (g->page_size - 1)) != 0)
+        return false;
+    if (g->pages_per_seq < 1 || g->pages_per_seq > (1 << 29) || g->num_pages < 1) return false;
+    return g->num_pages <= (int64_t)(0xFFFFFFFFu / (uint32_t)g->page_size);
+}
+
+int log2_exact(int32_t v) {
+    int k = 0;
+    while ((1 << k) < v) k++;
+    return k;
 }
 
 constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
@@ -986,19 +1111,23 @@ smla_status sparse_mla_combine(const float* o_part, const float* lse_part, int32
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
+// paged: NULL for a contiguous cache; then block_table is not used.
 static smla_status prepare(const void* q, const void* kv_cache, const int32_t* topk_idx,
                            const int32_t* seqlens, float scale, const smla_shape* shape,
+                           const smla_paged* paged, const int32_t* block_table,
                            DecodeArgs* a, Plan* p, bool* nothing) {
     *nothing = false;
     if (!shape) return SMLA_ERR_NULL;
-    if (!shape_ok(shape)) return SMLA_ERR_SHAPE;
+    if (!shape_ok(shape) || (paged && !paged_ok(paged))) return SMLA_ERR_SHAPE;
     if (shape->batch == 0 || shape->num_heads == 0) {   // nothing to touch
         *nothing = true;
         return SMLA_OK;
     }
     if (!q || !seqlens) return SMLA_ERR_NULL;
     if (shape->topk > 0 && (!kv_cache || !topk_idx)) return SMLA_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(topk_idx, 4) || !aligned(seqlens, 4))
+    if (paged && shape->topk > 0 && !block_table) return SMLA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(topk_idx, 4) || !aligned(seqlens, 4) ||
+        !aligned(block_table, 4))
         return SMLA_ERR_ALIGN;
     *p = make_plan(shape);
     memset(a, 0, sizeof(*a));
@@ -1014,8 +1143,16 @@ static smla_status prepare(const void* q, const void* kv_cache, const int32_t* t
     a->nsplit = p->nsplit;
     a->chunk = p->chunk;
     a->n_hb = p->n_hb;
-    a->seq_bytes = (uint32_t)(shape->kv_seq_stride * row_bytes_of(shape->row_format));
     a->row_format = shape->row_format;
+    if (paged) {
+        a->block_table = block_table;
+        a->page_shift = log2_exact(paged->page_size);
+        a->pages_per_seq = paged->pages_per_seq;
+        a->pool_rows = (uint32_t)(paged->num_pages << a->page_shift);
+        if (shape->topk == 0) a->block_table = nullptr;   // nothing is gathered
+    } else {
+        a->seq_bytes = (uint32_t)(shape->kv_seq_stride * row_bytes_of(shape->row_format));
+    }
     return SMLA_OK;
 }
 
@@ -1023,21 +1160,26 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const int grid = a.batch * p.n_hb * p.nsplit;
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    if (a.row_format == SMLA_ROW_UE8M0_SCALES)
-        hipLaunchKernelGGL(smla_decode_kernel<SMLA_ROW_UE8M0_SCALES>, dim3(grid), dim3(64 * kWaves), 0, hs, args);
-    else
-        hipLaunchKernelGGL(smla_decode_kernel<SMLA_ROW_FP32_SCALES>, dim3(grid), dim3(64 * kWaves), 0, hs, args);
+    const dim3 g(grid), blk(64 * kWaves);
+    const bool paged = a.block_table != nullptr;
+    if (a.row_format == SMLA_ROW_UE8M0_SCALES) {
+        if (paged) hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, true>), g, blk, 0, hs, args);
+        else hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args);
+    } else {
+        if (paged) hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, true>), g, blk, 0, hs, args);
+        else hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args);
+    }
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
-smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* topk_idx,
-                              const int32_t* seqlens, float scale, void* out, float* lse,
-                              const smla_shape* shape, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+static smla_status decode_impl(const void* q, const void* kv_cache, const int32_t* block_table,
+                               const int32_t* topk_idx, const int32_t* seqlens, float scale, void* out,
+                               float* lse, const smla_shape* shape, const smla_paged* paged,
+                               void* workspace, size_t workspace_bytes, void* stream) {
     DecodeArgs a;
     Plan p;
     bool nothing;
-    smla_status st = prepare(q, kv_cache, topk_idx, seqlens, scale, shape, &a, &p, &nothing);
+    smla_status st = prepare(q, kv_cache, topk_idx, seqlens, scale, shape, paged, block_table, &a, &p, &nothing);
     if (st != SMLA_OK || nothing) return st;
     if (!out || !lse) return SMLA_ERR_NULL;
     if (!aligned(out, 16) || !aligned(lse, 4)) return SMLA_ERR_ALIGN;
@@ -1067,13 +1209,14 @@ smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t
     return SMLA_OK;
 }
 
-smla_status sparse_mla_decode_partials(const void* q, const void* kv_cache, const int32_t* topk_idx,
-                                       const int32_t* seqlens, float scale, const smla_shape* shape,
-                                       float* o_part, float* lse_part, void* stream) {
+static smla_status partials_impl(const void* q, const void* kv_cache, const int32_t* block_table,
+                                 const int32_t* topk_idx, const int32_t* seqlens, float scale,
+                                 const smla_shape* shape, const smla_paged* paged, float* o_part,
+                                 float* lse_part, void* stream) {
     DecodeArgs a;
     Plan p;
     bool nothing;
-    smla_status st = prepare(q, kv_cache, topk_idx, seqlens, scale, shape, &a, &p, &nothing);
+    smla_status st = prepare(q, kv_cache, topk_idx, seqlens, scale, shape, paged, block_table, &a, &p, &nothing);
     if (st != SMLA_OK || nothing) return st;
     if (!o_part || !lse_part) return SMLA_ERR_NULL;
     if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return SMLA_ERR_ALIGN;
@@ -1083,6 +1226,39 @@ smla_status sparse_mla_decode_partials(const void* q, const void* kv_cache, cons
     a.lse_part = lse_part;
     a.force_partials = 1;
     return launch(a, p, (hipStream_t)stream);
+}
+
+smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                              const int32_t* seqlens, float scale, void* out, float* lse,
+                              const smla_shape* shape, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    return decode_impl(q, kv_cache, nullptr, topk_idx, seqlens, scale, out, lse, shape, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+smla_status sparse_mla_decode_partials(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                                       const int32_t* seqlens, float scale, const smla_shape* shape,
+                                       float* o_part, float* lse_part, void* stream) {
+    return partials_impl(q, kv_cache, nullptr, topk_idx, seqlens, scale, shape, nullptr, o_part, lse_part,
+                         stream);
+}
+
+smla_status sparse_mla_decode_paged(const void* q, const void* kv_pool, const int32_t* block_table,
+                                    const int32_t* topk_idx, const int32_t* seqlens, float scale, void* out,
+                                    float* lse, const smla_shape* shape, const smla_paged* paged,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!paged) return SMLA_ERR_NULL;
+    return decode_impl(q, kv_pool, block_table, topk_idx, seqlens, scale, out, lse, shape, paged, workspace,
+                       workspace_bytes, stream);
+}
+
+smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool, const int32_t* block_table,
+                                             const int32_t* topk_idx, const int32_t* seqlens, float scale,
+                                             const smla_shape* shape, const smla_paged* paged, float* o_part,
+                                             float* lse_part, void* stream) {
+    if (!paged) return SMLA_ERR_NULL;
+    return partials_impl(q, kv_pool, block_table, topk_idx, seqlens, scale, shape, paged, o_part, lse_part,
+                         stream);
 }
 
 int32_t smla_split_size(const smla_shape* shape) {

@@ -149,3 +149,32 @@ def test_shape_struct_matches_header(tmp_path):
     S = smla.SmlaShape
     assert [int(x) for x in got] == [ctypes.sizeof(S), S.num_splits.offset, S.kv_seq_stride.offset,
                                      S.row_format.offset]
+
+
+def _call_paged(L, shape, paged, ptrs=None):
+    p = ptrs or {}
+    fake = ctypes.c_void_p(1 << 20)
+    args = [p.get(n, fake) for n in ("q", "kv", "bt", "idx", "seqlens")]
+    return L.sparse_mla_decode_paged(*args, ctypes.c_float(0.05), p.get("out", fake), p.get("lse", fake),
+                                     ctypes.byref(shape), ctypes.byref(paged) if paged is not None else None,
+                                     None, ctypes.c_size_t(0), None)
+
+
+@needs_lib
+def test_paged_argument_errors_before_any_device_work():
+    L = smla.lib()
+    good = smla.make_shape(2, 16, 64, 1, 1)
+    pg = smla.make_paged(64, 8, 100)
+    assert _call_paged(L, good, None) == 1                            # NULL geometry
+    assert _call_paged(L, good, pg, {"bt": None}) == 1                # NULL block table
+    for bad in (smla.make_paged(48, 8, 100),                          # page size not a power of two
+                smla.make_paged(0, 8, 100), smla.make_paged(1 << 21, 8, 100),
+                smla.make_paged(64, 0, 100), smla.make_paged(64, 8, 0),
+                smla.make_paged(64, 8, (1 << 26))):                  # pool rows reach 2^32
+        assert _call_paged(L, good, bad) == 2
+    assert _call_paged(L, good, smla.make_paged(64, 8, (1 << 26) - 1)) in (7, 0)   # largest pool: valid
+    assert _call_paged(L, good, pg, {"bt": ctypes.c_void_p((1 << 20) + 2)}) == 6   # misaligned table
+    assert _call_paged(L, smla.make_shape(2, 16, 64, 1, 1, 3), pg) == 2             # unknown row format
+    import torch
+    if not torch.cuda.is_available():
+        assert _call_paged(L, good, pg) == 7                          # valid, but no device here
