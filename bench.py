@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=3, help="workload number 1..5 (default 3)")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--kernel", default="shared", choices=("shared", "per-head"),
+                    help="shared: the decode path; per-head: the per-head SIMT ablation kernel")
     ap.add_argument("--page-size", type=int, default=0,
                     help="0 = contiguous cache; else rows in a shuffled paged pool of this page size")
     ap.add_argument("--row-format", type=int, default=0, choices=(0, 1),
@@ -186,6 +188,12 @@ def main():
                               ctypes.byref(shape), wsp, ctypes.c_size_t(need_ws), hs))
     decode_fn = L.sparse_mla_decode_paged if paged else L.sparse_mla_decode
     partials_fn = L.sparse_mla_decode_partials_paged if paged else L.sparse_mla_decode_partials
+    if args.kernel == "per-head":
+        assert not paged, "the per-head ablation kernel reads a contiguous cache"
+        ns = 1
+        full_args = [(P(q), P(cache), P(idx), P(sl), ctypes.c_float(w.scale), P(out), P(lse), ctypes.byref(shape), hs)
+                     for q, cache, idx, sl, _ in sets]
+        decode_fn = L.sparse_mla_decode_per_head
 
     def step(i):
         """One whole step: decode kernel, then the combine kernel when split."""
@@ -281,6 +289,7 @@ def main():
                    "num_splits": ns, "split_size": chunk, "rotation": R,
                    "row_format": "ue8m0_scales_584B" if fmt == 1 else "fp32_scales_640B",
                    "cache": f"paged, {args.page_size} rows per page" if paged else "contiguous per sequence",
+                   "kernel": "per-head SIMT ablation" if args.kernel == "per-head" else "shared-read MFMA",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": None if paged else counted_traffic(args.config, fmt)},

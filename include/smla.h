@@ -198,6 +198,22 @@ smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool,
                                              const smla_shape* shape, const smla_paged* paged,
                                              float* o_part, float* lse_part, void* stream);
 
+/*
+ * sparse_mla_decode_per_head -- the same step computed the way the production
+ * kernel that the shared-read design replaced did it ("The Moment of
+ * Compilation", section "The Context: A Kernel Optimization Campaign"): one
+ * program (wave) per (sequence, head), fp32 vector arithmetic, every selected
+ * row read again for every head, no split of the list.  An ablation baseline
+ * for measuring the shared read; not the fast path.
+ *
+ *   arguments as for sparse_mla_decode; shape->num_splits is ignored and no
+ *   workspace is used.  Same numerical contract (fp32 logits from exact
+ *   operands; the value sum in fp32) and the same results up to rounding.
+ */
+smla_status sparse_mla_decode_per_head(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                                       const int32_t* seqlens, float scale, void* out, float* lse,
+                                       const smla_shape* shape, void* stream);
+
 /* List entries per split (C above, a multiple of 32); -1 for an invalid shape. */
 int32_t smla_split_size(const smla_shape* shape);
 

@@ -30,7 +30,7 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine",
-           "sparse_mla_decode_paged", "sparse_mla_decode_partials_paged",
+           "sparse_mla_decode_paged", "sparse_mla_decode_partials_paged", "sparse_mla_decode_per_head",
            "smla_workspace_bytes", "smla_num_splits", "smla_split_size", "smla_status_str")
 
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_decode.restype = ctypes.c_int
         L.sparse_mla_combine.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.sparse_mla_combine.restype = ctypes.c_int
+        L.sparse_mla_decode_per_head.argtypes = [vp, vp, vp, vp, f32, vp, vp, shp, vp]
+        L.sparse_mla_decode_per_head.restype = ctypes.c_int
         pgd = ctypes.POINTER(SmlaPaged)
         L.sparse_mla_decode_paged.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, shp, pgd, vp, ctypes.c_size_t, vp]
         L.sparse_mla_decode_paged.restype = ctypes.c_int
@@ -228,3 +230,18 @@ def sparse_mla_decode_partials_paged(q, kv_pool, block_table, topk_idx, seqlens,
                                                   ctypes.byref(paged), _ptr(o_part), _ptr(lse_part),
                                                   _stream_handle(stream)))
     return o_part, lse_part
+
+
+def sparse_mla_decode_per_head(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, kv_seq_stride=None,
+                               stream=None, row_format=0):
+    """The per-head SIMT ablation kernel (one wave per (sequence, head), rows
+    re-read per head); arguments as for sparse_mla_decode."""
+    B, H, _ = q.shape
+    topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    if kv_seq_stride is None:
+        kv_seq_stride = _seq_stride(kv_cache, B, row_format)
+    shape = make_shape(B, H, topk, 0, kv_seq_stride, row_format)
+    _check(lib().sparse_mla_decode_per_head(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(seqlens),
+                                            ctypes.c_float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape),
+                                            _stream_handle(stream)))
+    return out, lse

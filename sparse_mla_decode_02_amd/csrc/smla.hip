@@ -65,6 +65,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
@@ -955,6 +956,135 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-head SIMT decode: the ablation baseline.  The production kernel that the
+// shared-read rewrite replaced ("The Moment of Compilation", section "The
+// Context: A Kernel Optimization Campaign"; "The Power-of-Two Trap", section
+// "The Scene") ran one program per head in f32 on the vector units and read
+// every selected row again for every head.  This is that design on gfx950: one
+// wave per (sequence, head), lane l holding latent columns 8l..8l+7 (l < 56:
+// fp8 codes of group l / 8 with its scale; l >= 56: rope), one row at a time
+// through global loads, q . K reduced across the wave, an online softmax in
+// fp32, no split of the list.  Same results as the main path (fp32 logits from
+// exact operands), different cost: each row is read H times.
+struct PerHeadArgs {
+    const uint16_t* q;
+    const uint8_t* kv;
+    const int32_t* idx;
+    const int32_t* seqlens;
+    uint16_t* out;
+    float* lse;
+    int64_t kv_seq_stride;
+    float logit_factor;   // scale * log2(e)
+    int32_t batch, heads, topk;
+    int32_t row_format;   // host only
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+    return x;
+}
+
+template <int F>
+__global__ __launch_bounds__(256) void smla_per_head_kernel(PerHeadArgs a) {
+    constexpr int RB = RowFormat<F>::kBytes;
+    const int lane = threadIdx.x & 63;
+    const int bh = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+    if (bh >= a.batch * a.heads) return;
+    const int b = bh / a.heads;
+    const bool rope = lane >= 56;
+
+    float qv[8];
+    {
+        const u32x4 qq = *(const u32x4*)(a.q + (int64_t)bh * kLatent + 8 * lane);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            qv[2 * k] = __uint_as_float(qq[k] << 16);
+            qv[2 * k + 1] = __uint_as_float(qq[k] & 0xFFFF0000u);
+        }
+    }
+    const uint8_t* seq = a.kv + (int64_t)b * a.kv_seq_stride * RB;
+    const int32_t* list = a.idx + (int64_t)b * a.topk;
+    const int seqlen = a.seqlens[b];
+    const int off = rope ? RowFormat<F>::kRopeOff + 16 * (lane - 56) : 8 * lane;
+
+    // this lane's 8 dequantised columns of a row
+    auto load_row = [&](int t, float (&K)[8]) {
+        const uint8_t* row = seq + (int64_t)t * RB;
+        const u32x2 lo = *(const u32x2*)(row + off);
+        if (rope) {
+            const u32x2 hi = *(const u32x2*)(row + off + 8);
+            const uint32_t w[4] = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                K[2 * k] = __uint_as_float(w[k] << 16);
+                K[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            }
+        } else {
+            float sc;
+            if constexpr (F == SMLA_ROW_UE8M0_SCALES) sc = ue8m0_value(row[SMLA_SCALE_OFFSET + (lane >> 3)]);
+            else sc = *(const float*)(row + SMLA_SCALE_OFFSET + 4 * (lane >> 3));
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                const f32x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo[k], 1.0f, false);
+                const f32x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo[k], 1.0f, true);
+                K[4 * k] = c0[0] * sc;
+                K[4 * k + 1] = c0[1] * sc;
+                K[4 * k + 2] = c1[0] * sc;
+                K[4 * k + 3] = c1[1] * sc;
+            }
+        }
+    };
+
+    float m = -INFINITY, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    constexpr int kU = 4;   // rows in flight per step
+    for (int j0 = 0; j0 < a.topk; j0 += kU) {
+        int t[kU];
+        bool ok[kU];
+        float K[kU][8], z[kU];
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            t[u] = j0 + u < a.topk ? list[j0 + u] : -1;
+            ok[u] = t[u] >= 0 && t[u] < seqlen;
+            if (ok[u]) load_row(t[u], K[u]);
+            else
+#pragma unroll
+                for (int k = 0; k < 8; k++) K[u][k] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            float d = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; k++) d += qv[k] * K[u][k];
+            z[u] = wave_sum(d);
+            z[u] = ok[u] ? z[u] * a.logit_factor : -INFINITY;
+        }
+        float mx = m;
+#pragma unroll
+        for (int u = 0; u < kU; u++) mx = fmaxf(mx, z[u]);
+        if (mx == -INFINITY) continue;   // nothing kept so far
+        const float alpha = __builtin_amdgcn_exp2f(m - mx);
+        l *= alpha;
+#pragma unroll
+        for (int k = 0; k < 8; k++) o[k] *= alpha;
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const float p = __builtin_amdgcn_exp2f(z[u] - mx);
+            l += p;
+#pragma unroll
+            for (int k = 0; k < 8; k++) o[k] += p * K[u][k];
+        }
+        m = mx;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    u32x4 pk;
+#pragma unroll
+    for (int k = 0; k < 4; k++) pk[k] = pack_bf16x2(o[2 * k] * inv, o[2 * k + 1] * inv);
+    *(u32x4*)(a.out + (int64_t)bh * kLatent + 8 * lane) = pk;
+    if (lane == 0) a.lse[bh] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
 struct Plan {
     int n_hb;     // 16-head blocks (workgroups per sequence and split)
     int nsplit;
@@ -1259,6 +1389,40 @@ smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool,
     if (!paged) return SMLA_ERR_NULL;
     return partials_impl(q, kv_pool, block_table, topk_idx, seqlens, scale, shape, paged, o_part, lse_part,
                          stream);
+}
+
+smla_status sparse_mla_decode_per_head(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                                       const int32_t* seqlens, float scale, void* out, float* lse,
+                                       const smla_shape* shape, void* stream) {
+    DecodeArgs d;
+    Plan p;
+    bool nothing;
+    smla_status st = prepare(q, kv_cache, topk_idx, seqlens, scale, shape, nullptr, nullptr, &d, &p, &nothing);
+    if (st != SMLA_OK || nothing) return st;
+    if (!out || !lse) return SMLA_ERR_NULL;
+    if (!aligned(out, 16) || !aligned(lse, 4)) return SMLA_ERR_ALIGN;
+    st = device_check();
+    if (st != SMLA_OK) return st;
+    PerHeadArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = (const uint16_t*)q;
+    a.kv = (const uint8_t*)kv_cache;
+    a.idx = topk_idx;
+    a.seqlens = seqlens;
+    a.out = (uint16_t*)out;
+    a.lse = lse;
+    a.kv_seq_stride = shape->kv_seq_stride;
+    a.logit_factor = scale * kLog2e;
+    a.batch = shape->batch;
+    a.heads = shape->num_heads;
+    a.topk = shape->topk;
+    const int rows = shape->batch * shape->num_heads;
+    const dim3 g((rows + 3) / 4), blk(256);
+    if (shape->row_format == SMLA_ROW_UE8M0_SCALES)
+        hipLaunchKernelGGL(smla_per_head_kernel<SMLA_ROW_UE8M0_SCALES>, g, blk, 0, (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(smla_per_head_kernel<SMLA_ROW_FP32_SCALES>, g, blk, 0, (hipStream_t)stream, a);
+    return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
 int32_t smla_split_size(const smla_shape* shape) {

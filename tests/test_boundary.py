@@ -178,3 +178,20 @@ def test_paged_argument_errors_before_any_device_work():
     import torch
     if not torch.cuda.is_available():
         assert _call_paged(L, good, pg) == 7                          # valid, but no device here
+
+
+@needs_lib
+def test_per_head_argument_errors():
+    L = smla.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    good = smla.make_shape(2, 16, 64, 0, 128)
+
+    def call(shape, **over):
+        a = dict(q=fake, kv=fake, idx=fake, sl=fake, out=fake, lse=fake)
+        a.update(over)
+        return L.sparse_mla_decode_per_head(a["q"], a["kv"], a["idx"], a["sl"], ctypes.c_float(0.05), a["out"],
+                                            a["lse"], ctypes.byref(shape) if shape is not None else None, None)
+    assert call(None) == 1
+    assert call(good, out=None) == 1
+    assert call(smla.make_shape(2, 20, 64, 0, 128)) == 2
+    assert call(good, out=ctypes.c_void_p((1 << 20) + 8)) == 6
