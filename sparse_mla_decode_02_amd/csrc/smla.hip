@@ -1009,26 +1009,39 @@ __global__ __launch_bounds__(256) void smla_per_head_kernel(PerHeadArgs a) {
     const int seqlen = a.seqlens[b];
     const int off = rope ? RowFormat<F>::kRopeOff + 16 * (lane - 56) : 8 * lane;
 
-    // this lane's 8 dequantised columns of a row
-    auto load_row = [&](int t, float (&K)[8]) {
+    // this lane's bytes of a row: 8 code bytes and the group scale, or 16 rope bytes
+    auto load_raw = [&](int t) -> u32x4 {
         const uint8_t* row = seq + (int64_t)t * RB;
         const u32x2 lo = *(const u32x2*)(row + off);
+        u32x4 r;
+        r[0] = lo[0];
+        r[1] = lo[1];
         if (rope) {
             const u32x2 hi = *(const u32x2*)(row + off + 8);
-            const uint32_t w[4] = {lo[0], lo[1], hi[0], hi[1]};
+            r[2] = hi[0];
+            r[3] = hi[1];
+        } else {
+            if constexpr (F == SMLA_ROW_UE8M0_SCALES)
+                r[2] = __float_as_uint(ue8m0_value(row[SMLA_SCALE_OFFSET + (lane >> 3)]));
+            else r[2] = *(const uint32_t*)(row + SMLA_SCALE_OFFSET + 4 * (lane >> 3));
+            r[3] = 0;
+        }
+        return r;
+    };
+    // its 8 dequantised columns
+    auto dequant = [&](const u32x4& r, float (&K)[8]) {
+        if (rope) {
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                K[2 * k] = __uint_as_float(w[k] << 16);
-                K[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+                K[2 * k] = __uint_as_float(r[k] << 16);
+                K[2 * k + 1] = __uint_as_float(r[k] & 0xFFFF0000u);
             }
         } else {
-            float sc;
-            if constexpr (F == SMLA_ROW_UE8M0_SCALES) sc = ue8m0_value(row[SMLA_SCALE_OFFSET + (lane >> 3)]);
-            else sc = *(const float*)(row + SMLA_SCALE_OFFSET + 4 * (lane >> 3));
+            const float sc = __uint_as_float(r[2]);
 #pragma unroll
             for (int k = 0; k < 2; k++) {
-                const f32x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo[k], 1.0f, false);
-                const f32x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo[k], 1.0f, true);
+                const f32x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[k], 1.0f, false);
+                const f32x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[k], 1.0f, true);
                 K[4 * k] = c0[0] * sc;
                 K[4 * k + 1] = c0[1] * sc;
                 K[4 * k + 2] = c1[0] * sc;
@@ -1037,29 +1050,32 @@ __global__ __launch_bounds__(256) void smla_per_head_kernel(PerHeadArgs a) {
         }
     };
 
+    // kU rows in flight per step: their raw bytes are loaded together, the
+    // logits reduced together, and each row is dequantised again for the
+    // value sum (registers rather than memory traffic)
     float m = -INFINITY, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    constexpr int kU = 4;   // rows in flight per step
+    constexpr int kU = 8;
     for (int j0 = 0; j0 < a.topk; j0 += kU) {
-        int t[kU];
         bool ok[kU];
-        float K[kU][8], z[kU];
+        u32x4 raw[kU];
+        float z[kU];
 #pragma unroll
         for (int u = 0; u < kU; u++) {
-            t[u] = j0 + u < a.topk ? list[j0 + u] : -1;
-            ok[u] = t[u] >= 0 && t[u] < seqlen;
-            if (ok[u]) load_row(t[u], K[u]);
-            else
-#pragma unroll
-                for (int k = 0; k < 8; k++) K[u][k] = 0.f;
+            const int t = j0 + u < a.topk ? list[j0 + u] : -1;
+            ok[u] = t >= 0 && t < seqlen;
+            raw[u] = ok[u] ? load_raw(t) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kU; u++) {
+            float K[8];
+            dequant(raw[u], K);
             float d = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; k++) d += qv[k] * K[u][k];
-            z[u] = wave_sum(d);
-            z[u] = ok[u] ? z[u] * a.logit_factor : -INFINITY;
+            for (int k = 0; k < 8; k++) d += qv[k] * K[k];
+            z[u] = d;
         }
+#pragma unroll
+        for (int u = 0; u < kU; u++) z[u] = ok[u] ? wave_sum(z[u]) * a.logit_factor : -INFINITY;
         float mx = m;
 #pragma unroll
         for (int u = 0; u < kU; u++) mx = fmaxf(mx, z[u]);
@@ -1072,8 +1088,10 @@ __global__ __launch_bounds__(256) void smla_per_head_kernel(PerHeadArgs a) {
         for (int u = 0; u < kU; u++) {
             const float p = __builtin_amdgcn_exp2f(z[u] - mx);
             l += p;
+            float K[8];
+            dequant(raw[u], K);
 #pragma unroll
-            for (int k = 0; k < 8; k++) o[k] += p * K[u][k];
+            for (int k = 0; k < 8; k++) o[k] += p * K[k];
         }
         m = mx;
     }
