@@ -104,7 +104,6 @@ constexpr int kScaleGathers = 4;                      // 4-byte gathers of the s
 constexpr int kWaves = 4;                             // waves per workgroup (one per SIMD)
 constexpr int kAccBytes = 32 * 64 * 16;               // one wave's output accumulator (32 KB)
 constexpr int kWaveLds = 2 * kSlot;                   // two tile slots per wave
-constexpr int kStat = kWaves * kAccBytes;             // merge statistics, after the merge buffers
 constexpr int kLdsBytes = kWaves * kWaveLds;          // 152 KB
 
 // Byte layout of a cache row in each format (include/smla.h).  Both keep the
@@ -128,7 +127,7 @@ struct RowFormat<SMLA_ROW_UE8M0_SCALES> {
 // into the fp32 table rows 0..6 before the tile is computed.
 constexpr int kScaleRaw = kScaleTable + 4 * kTile * 4;
 
-static_assert(kStat + kWaves * 32 * 4 <= kLdsBytes, "merge buffers and statistics reuse the slots");
+static_assert(kAccBytes + 32 * 4 <= kWaveLds, "a wave's accumulator and statistics fit in its own slots");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 
 __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t lo, uint32_t hi) {
@@ -893,32 +892,36 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     }
     wait_vmcnt<0>();
 
-    // ---------------- merge of the four waves' states
+    // ---------------- merge of the four waves' states.  Each wave stores its
+    // accumulator (unscaled, straight from its AGPRs) and its statistics into
+    // its own two tile slots, which no other wave touches, as soon as its last
+    // tile is done; one barrier then makes the four visible to all.
     const float l_tot = lanegroup_sum(l_run);
-    __syncthreads();   // every wave is done with its slots (the merge reuses them)
-    lds_f32* stat = (lds_f32*)(lds + kStat);   // [wave][max 16 | sum 16]
-    if (lane < 16) {
-        stat[wave * 32 + lane] = m_run;
-        stat[wave * 32 + 16 + lane] = l_tot;
+    {
+        lds_u8* const mine = lds + wave * kWaveLds;
+        lds_f32x4* part = (lds_f32x4*)mine;
+#pragma unroll
+        for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i];
+        lds_f32* stat = (lds_f32*)(mine + kAccBytes);   // [max 16 | sum 16]
+        if (lane < 16) {
+            stat[lane] = m_run;
+            stat[16 + lane] = l_tot;
+        }
     }
     __syncthreads();
+    auto stat_of = [&](int w) { return (lds_cf32*)(lds + w * kWaveLds + kAccBytes); };
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, stat[w * 32 + ln]);
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, stat_of(w)[ln]);
     const float Ms0 = M == -INFINITY ? 0.f : M;
     // weight of wave w's accumulator for head ln: 2^(m_w - M)
     float wgt[kWaves];
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; w++) {
-        wgt[w] = __builtin_amdgcn_exp2f(stat[w * 32 + ln] - Ms0);
-        L += wgt[w] * stat[w * 32 + 16 + ln];
+        wgt[w] = __builtin_amdgcn_exp2f(stat_of(w)[ln] - Ms0);
+        L += wgt[w] * stat_of(w)[16 + ln];
     }
-    // the accumulators go to LDS unscaled, straight from their AGPRs
-    lds_f32x4* part = (lds_f32x4*)(lds + wave * kAccBytes);
-#pragma unroll
-    for (int i = 0; i < 32; i++) part[i * 64 + lane] = acc_o[i];
-    __syncthreads();
 
     // wave w finishes accumulator blocks 8w..8w+7; block i holds columns
     // 16i + 4qg + j for head ln
@@ -931,7 +934,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     auto block_sum = [&](int i) -> f32x4 {   // the normalised output block
         f32x4 v = wgt[0] * ((lds_cf32x4*)lds)[i * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kWaves; w++) v += wgt[w] * ((lds_cf32x4*)(lds + w * kAccBytes))[i * 64 + lane];
+        for (int w = 1; w < kWaves; w++) v += wgt[w] * ((lds_cf32x4*)(lds + w * kWaveLds))[i * 64 + lane];
         return v;
     };
     const int i0 = wave * (32 / kWaves);
