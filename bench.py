@@ -53,6 +53,14 @@ COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "decode_b32_h64_s32768_k512_ker
 COUNTER_CONFIG = 3
 
 
+def code_digest(source: str) -> str:
+    """sha256[:16] of a C++ source with its // and /* */ comments and blank
+    lines removed: it changes when the code does, not when a comment does."""
+    source = re.sub(r"/\*.*?\*/", "", source, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in source.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln.strip()).encode()).hexdigest()[:16]
+
+
 def counted_traffic(config, row_format):
     """HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE, calibrated against a
     plain device copy) from the committed rocprofv3 counter summary, when that
@@ -62,8 +70,8 @@ def counted_traffic(config, row_format):
         return None
     text = open(COUNTER_SUMMARY).read()
     src = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc", "smla.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    m_src = re.search(r"sha256\[:16\] = ([0-9a-f]{16})", text)
+    digest = code_digest(open(src).read())
+    m_src = re.search(r"code sha256\[:16\] = ([0-9a-f]{16})", text)
     m_dec = re.search(r"decode kernel: FETCH_SIZE .*?-> ([0-9.]+) MB per launch; WRITE_SIZE .*?-> ([0-9.]+) MB", text)
     if not m_src or not m_dec or m_src.group(1) != digest:
         return None

@@ -1,5 +1,6 @@
 // Sparse MLA decode for AMD CDNA4 (gfx950): split-K decode kernel, log-sum-exp
-// combine kernel, and the C ABI declared in include/smla.h.
+// combine kernel, the per-head ablation kernel, and the C ABI declared in
+// include/smla.h.
 //
 // What is computed ("The Moment of Compilation", section "The Context: A Kernel
 // Optimization Campaign"; "The Power-of-Two Trap", sections "The Scene" and
@@ -19,10 +20,16 @@
 //    latent: it owns two 32-token LDS slots, gathers its next tile straight
 //    into one (buffer_load_dwordx4 with the lds bit, 16 bytes per lane,
 //    coalesced along the row) while it computes the current one from the
-//    other, and never waits for another wave until the end.  A workgroup is four such waves (one per
-//    SIMD, the whole 160 KB LDS) on the same (sequence, head group, split);
-//    they take the split's tiles round robin and merge their online-softmax
-//    states once, through LDS, at the end.
+//    other, and never waits for another wave until the end.  A workgroup is
+//    four such waves (one per SIMD, 152 KB of the 160 KB LDS) on the same
+//    (sequence, head group, split); they take the split's tiles round robin
+//    and merge their online-softmax states once, through LDS, at the end.
+//  * Rows come from a cache contiguous per sequence (a buffer resource per
+//    sequence, 32-bit row offsets, the range check zero-filling masked rows)
+//    or from a paged pool of any size through a block table (64-bit
+//    global_load_lds gathers, masked rows from a zero row); in either row
+//    format, fp32 group scales (640-byte rows) or UE8M0 exponent bytes
+//    (584-byte rows, expanded to the same fp32 scale table in LDS).
 //  * QK^T runs as S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: the fp8 codes are
 //    converted exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with unit scale),
 //    q is used as stored, and each 64-column group's fp32 scale multiplies that
@@ -218,8 +225,9 @@ __device__ __forceinline__ uint64_t mask_by_token(uint64_t by_pos) {
 // Buffer resource over one sequence's cache rows (gfx9 raw buffer, stride 0):
 // a gather addresses a row by a 32-bit byte offset, and the hardware range
 // check turns every offset at or past `bytes` into a load of zeros.  A masked
-// list entry therefore uses row -1: its offset is negative, i.e. above 2^32 -
-// 640 as an unsigned number, and it stages zeros (finite, contributes nothing).
+// list entry therefore uses row -1: its offset is negative, i.e. above 2^32
+// minus the row bytes as an unsigned number, and it stages zeros (finite,
+// contributes nothing).
 __device__ __forceinline__ i32x4 row_rsrc(const uint8_t* base, uint32_t bytes) {
     const uint64_t p = (uint64_t)base;
     i32x4 r;
