@@ -249,6 +249,17 @@ def main():
     # alone for the decode kernel's own average duration
     ms_per_step, wall_ms = timed(step, args.steps)
     dec_ms, _ = timed(decode_only, args.steps)
+    # secondary, labelled: the same inputs every step (last-level cache warm),
+    # and each step's own duration (events around every step, rotated inputs)
+    warm_ms, _ = timed(lambda i: step(0), args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
     comb_ms = ms_per_step - dec_ms if ns > 1 else 0.0
     t_dec = dec_ms * 1e-3
     kv_bytes = ROW_ALGO_BYTES[fmt] * n_rows
@@ -305,6 +316,10 @@ def main():
         "effective_kv_gbps": kv_gbps,
         "all_algorithmic_gbps": all_bytes / t_dec / 1e9,
         "decode_us": t_dec * 1e6,
+        "step_us_percentiles": {"p10": float(np.percentile(per_step, 10)), "p50": float(np.median(per_step)),
+                                "p90": float(np.percentile(per_step, 90)),
+                                "note": "events around every step, rotated inputs"},
+        "warm_step_us": warm_ms * 1e3,
         "combine_us": comb_ms * 1e3,
         "mfma_tflops": flops / t_dec / 1e12,
         "mfma_frac": flops / t_dec / 1e12 / BF16_PEAK_TFLOPS,

@@ -103,10 +103,11 @@ size_t smla_workspace_bytes(const smla_shape* shape);
  *             584, formats above), 16-byte aligned; row t of sequence b
  *             starts at (b * kv_seq_stride + t) * R
  *   topk_idx  int32 [B][topk], 4-byte aligned: cache row of each list entry.
- *             An entry is skipped when it is < 0 or >= seqlens[b] (-1 pads
- *             short lists); entries may come in any order; a repeated entry
- *             is counted once per occurrence
- *   seqlens   int32 [B], 4-byte aligned; seqlens[b] <= kv_seq_stride
+ *             An entry is skipped when it is < 0, >= seqlens[b] or >=
+ *             kv_seq_stride (-1 pads short lists), so no device contents can
+ *             make a sequence read outside its own rows; entries may come in
+ *             any order; a repeated entry is counted once per occurrence
+ *   seqlens   int32 [B], 4-byte aligned (normally <= kv_seq_stride)
  *   scale     softmax scale applied to q . K (e.g. 1/sqrt(512))
  *   out       bf16 [B][H][512], 16-byte aligned:
  *             out = sum_j softmax_j(scale * q . K_j) * K_j over the kept entries;

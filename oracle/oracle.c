@@ -127,11 +127,15 @@ typedef struct {
 } cache_layout;
 
 /* Row of entry t of sequence b, or NULL when the entry is skipped: t < 0,
- * t >= seqlen, and (paged) a position past the sequence's block-table row or
- * a page id outside the pool. */
+ * t >= seqlen, (contiguous) t at or past the sequence stride, so that a
+ * sequence never reaches another's rows, and (paged) a position past the
+ * sequence's block-table row or a page id outside the pool. */
 static const uint8_t* row_of(const cache_layout* c, int b, int32_t t, int32_t seqlen) {
     if (t < 0 || t >= seqlen) return NULL;
-    if (!c->block_table) return c->base + ((int64_t)b * c->kv_seq_stride + t) * c->row_stride;
+    if (!c->block_table) {
+        if (t >= c->kv_seq_stride) return NULL;
+        return c->base + ((int64_t)b * c->kv_seq_stride + t) * c->row_stride;
+    }
     int64_t p = t / c->page_size;
     if (p >= c->pages_per_seq) return NULL;
     int64_t page = c->block_table[(int64_t)b * c->pages_per_seq + p];

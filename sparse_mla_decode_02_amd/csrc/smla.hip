@@ -756,7 +756,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     const int t_begin = split * a.chunk;
     const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
     const int ntiles = (n_ent + kTile - 1) / kTile;
-    const int seqlen = a.seqlens[b];
+    // contiguous cache: entries at or past the sequence stride are skipped too,
+    // so that a sequence never reaches another's rows
+    const int seqlen = P ? a.seqlens[b] : (int)min((int64_t)a.seqlens[b], a.kv_seq_stride);
     // contiguous cache: a buffer resource over the sequence's rows
     const i32x4 rsrc = P ? i32x4{0, 0, 0, 0}
                          : row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
@@ -1017,7 +1019,7 @@ __global__ __launch_bounds__(256) void smla_per_head_kernel(PerHeadArgs a) {
     }
     const uint8_t* seq = a.kv + (int64_t)b * a.kv_seq_stride * RB;
     const int32_t* list = a.idx + (int64_t)b * a.topk;
-    const int seqlen = a.seqlens[b];
+    const int seqlen = (int)min((int64_t)a.seqlens[b], a.kv_seq_stride);   // never past the stride
     const int off = rope ? RowFormat<F>::kRopeOff + 16 * (lane - 56) : 8 * lane;
 
     // this lane's bytes of a row: 8 code bytes and the group scale, or 16 rope bytes

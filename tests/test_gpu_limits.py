@@ -87,3 +87,29 @@ def test_largest_sequence_stride(row_format):
                 ref_lse, label=f"stride {stride} fmt{row_format} ns{ns}")
     del cache
     torch.cuda.empty_cache()
+
+
+def test_entries_past_the_stride_are_skipped():
+    # seqlens above the stride: the decode and the per-head kernels skip the
+    # entries at or past the stride instead of reading the next sequence
+    w = make_workload(seed=504, batch=3, heads=32, topk=96, seqlen=400, kv_seq_stride=400)
+    cache_h = build_host_cache(w)
+    idx_bad = w.idx.copy()
+    idx_bad[:, ::4] = 400 + np.arange(idx_bad[:, ::4].shape[1])[None, :]
+    idx_ref = idx_bad.copy()
+    idx_ref[:, ::4] = -1
+    ref_out, ref_lse, _ = oracle.decode_raw(w.q_bits, cache_h, 400, idx_ref, w.seqlens, w.heads, w.scale)
+    q, cache, _, _ = device_inputs(w)
+    idx = torch.from_numpy(idx_bad).to(DEV)
+    big = torch.full((3,), 10 ** 6, dtype=torch.int32, device=DEV)
+    for kernel, ns in (("decode", 1), ("decode", 3), ("per-head", 0)):
+        log(f"case: entries past the stride, {kernel} ns {ns}")
+        out = torch.full((3, 32, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((3, 32), float("nan"), device=DEV)
+        if kernel == "decode":
+            smla.sparse_mla_decode(q, cache, idx, big, w.scale, out, lse, num_splits=ns, kv_seq_stride=400)
+        else:
+            smla.sparse_mla_decode_per_head(q, cache, idx, big, w.scale, out, lse, kv_seq_stride=400)
+        torch.cuda.synchronize()
+        compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_out,
+                ref_lse, label=f"past stride {kernel} ns{ns}")

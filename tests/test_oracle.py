@@ -371,3 +371,19 @@ def test_paged_missing_pages_skip_their_entries():
                                            w.seqlens, w.heads, w.scale)
     assert np.array_equal(out.view(np.uint64), ref.view(np.uint64))
     assert np.array_equal(lse.view(np.uint64), rlse.view(np.uint64))
+
+
+def test_entries_past_the_stride_are_skipped():
+    # seqlens above the stride (a precondition violation) must not reach the
+    # next sequence's rows: entries at or past the stride count as masked
+    w = make_workload(seed=47, batch=3, heads=16, topk=40, seqlen=200, kv_seq_stride=200)
+    cache = build_host_cache(w)
+    idx2 = w.idx.copy()
+    idx2[:, ::5] = 200 + np.arange(idx2[:, ::5].shape[1])[None, :]
+    ref_idx = idx2.copy()
+    ref_idx[:, ::5] = -1
+    big = np.full(3, 10 ** 6, dtype=np.int32)
+    out, lse, _ = oracle.decode_raw(w.q_bits, cache, 200, idx2, big, w.heads, w.scale)
+    ref, rlse, _ = oracle.decode_raw(w.q_bits, cache, 200, ref_idx, w.seqlens, w.heads, w.scale)
+    assert np.array_equal(out.view(np.uint64), ref.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), rlse.view(np.uint64))
