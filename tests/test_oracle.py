@@ -183,12 +183,15 @@ def test_combine_all_empty():
     assert np.all(out == 0) and np.all(np.isneginf(lse))
 
 
-def test_golden_regression():
+@pytest.mark.parametrize("row_format,name", [(0, "oracle_cfg1.json"), (1, "oracle_cfg1_ue8m0.json")])
+def test_golden_regression(row_format, name):
     # values written by tests/golden/make_golden.py from the oracle
-    with open(os.path.join(GOLDEN, "oracle_cfg1.json")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         g = json.load(f)
-    w = config_workload(1)
-    out, lse, _ = run(w)
+    w = config_workload(1, row_format=row_format)
+    cache = build_host_cache(w)
+    out, lse, _ = oracle.decode_raw(w.q_bits, cache, w.kv_seq_stride, w.idx, w.seqlens, w.heads, w.scale,
+                                    row_format=row_format)
     assert np.allclose(lse.ravel(), np.array(g["lse"]), rtol=0, atol=1e-12)
     sample = out.reshape(-1)[np.array(g["out_index"])]
     assert np.allclose(sample, np.array(g["out_value"]), rtol=0, atol=1e-12)
