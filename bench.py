@@ -252,6 +252,13 @@ def main():
     # secondary, labelled: the same inputs every step (last-level cache warm),
     # and each step's own duration (events around every step, rotated inputs)
     warm_ms, _ = timed(lambda i: step(0), args.steps)
+    # KV cold, q / list / lengths warm: rotated caches, the first copy's other inputs
+    kvcold_args = []
+    for q, cache, idx, sl, bt in sets:
+        a = list(full_args[len(kvcold_args)])
+        a[0], a[2 if not paged else 3], a[3 if not paged else 4] = (P(sets[0][0]), P(sets[0][2]), P(sets[0][3]))
+        kvcold_args.append(tuple(a))
+    kvcold_ms, _ = timed(lambda i: decode_fn(*kvcold_args[i % R]), args.steps)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     evs[0].record(stream)
@@ -320,6 +327,7 @@ def main():
                                 "p90": float(np.percentile(per_step, 90)),
                                 "note": "events around every step, rotated inputs"},
         "warm_step_us": warm_ms * 1e3,
+        "kv_cold_q_warm_step_us": kvcold_ms * 1e3,
         "combine_us": comb_ms * 1e3,
         "mfma_tflops": flops / t_dec / 1e12,
         "mfma_frac": flops / t_dec / 1e12 / BF16_PEAK_TFLOPS,
