@@ -61,6 +61,15 @@ def code_digest(source: str) -> str:
     return hashlib.sha256("\n".join(ln for ln in lines if ln.strip()).encode()).hexdigest()[:16]
 
 
+def kernel_digest() -> str:
+    """code_digest of the library's kernel sources and the compiler flags they
+    are built with: what the machine code of the profiled kernels depends on."""
+    from sparse_mla_decode_02_amd import build as hip_build
+    csrc = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc")
+    text = "".join(open(os.path.join(csrc, f)).read() for f in sorted(os.listdir(csrc)) if f.endswith(".hip"))
+    return code_digest(text + "\n// flags: " + " ".join(hip_build.HIPCC_FLAGS + hip_build.VGPR_FORM))
+
+
 def counted_traffic(config, row_format):
     """HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE, calibrated against a
     plain device copy) from the committed rocprofv3 counter summary, when that
@@ -69,8 +78,7 @@ def counted_traffic(config, row_format):
     if config != COUNTER_CONFIG or row_format != 0 or not os.path.exists(COUNTER_SUMMARY):
         return None
     text = open(COUNTER_SUMMARY).read()
-    src = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc", "smla.hip")
-    digest = code_digest(open(src).read())
+    digest = kernel_digest()
     m_src = re.search(r"code sha256\[:16\] = ([0-9a-f]{16})", text)
     m_dec = re.search(r"decode kernel: FETCH_SIZE .*?-> ([0-9.]+) MB per launch; WRITE_SIZE .*?-> ([0-9.]+) MB", text)
     if not m_src or not m_dec or m_src.group(1) != digest:

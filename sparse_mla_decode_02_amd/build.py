@@ -9,6 +9,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "smla.hip")
+SRC_PAGED = os.path.join(HERE, "csrc", "smla_paged.hip")
 LIB = os.path.join(HERE, "libsmla.so")
 
 HIPCC_FLAGS = [
@@ -16,10 +17,14 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed fp32 arithmetic in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# MFMA results in VGPRs: the logit accumulators are read by vector
+# instructions right after their MFMAs, which otherwise copy them out of AGPRs
+# (64 instructions per tile).  Not for the paged instances (smla_paged.hip):
+# there it makes registers spill into AGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:
@@ -29,17 +34,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libsmla.so)")
 
 
-def build(verbose: bool = False, extra: list | None = None) -> str:
-    """Always recompiles; writes to a temporary file then renames atomically."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), SRC, "-o", tmp]
+def _run(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("building libsmla.so failed")
+        raise RuntimeError("building libsmla.so failed: " + " ".join(cmd[:1] + cmd[-3:]))
     if verbose:
         sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False, extra: list | None = None) -> str:
+    """Always recompiles (two objects, then one shared library); writes to a
+    temporary file then renames atomically."""
+    tag = "%d" % os.getpid()
+    tmp_dir = os.path.join(HERE, "_build_tmp" + tag)
+    os.makedirs(tmp_dir, exist_ok=True)
+    try:
+        obj_main = os.path.join(tmp_dir, "smla.o")
+        obj_paged = os.path.join(tmp_dir, "smla_paged.o")
+        _run([hipcc(), *HIPCC_FLAGS, *VGPR_FORM, *(extra or []), "-c", SRC, "-o", obj_main], verbose)
+        _run([hipcc(), *HIPCC_FLAGS, *(extra or []), "-c", SRC_PAGED, "-o", obj_paged], verbose)
+        tmp = LIB + ".tmp" + tag
+        _run([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", obj_main, obj_paged, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmp_dir, ignore_errors=True)
     return LIB
 
 

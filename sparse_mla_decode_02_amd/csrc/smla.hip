@@ -708,6 +708,7 @@ __device__ __forceinline__ void combine_row(const float* o_part, const float* ls
     if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
+#ifndef SMLA_PAGED_TU
 // The combine as its own kernel: one wave per (b, h), four rows per
 // workgroup.  When the grid is a multiple of 8, workgroup ids are remapped like
 // the decode kernel's, so that XCD x merges the rows of the same contiguous
@@ -722,6 +723,7 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
     if (row >= rows) return;
     combine_row(o_part, lse_part, row, nsplit, out, lse, threadIdx.x & 63);
 }
+#endif
 
 // Paged pool: the page ids of a tile's entries, 32 per wave and slot, after
 // the tile slots.
@@ -1116,6 +1118,7 @@ __global__ __launch_bounds__(256) void smla_per_head_kernel(PerHeadArgs a) {
     if (lane == 0) a.lse[bh] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
+#ifndef SMLA_PAGED_TU
 struct Plan {
     int n_hb;     // 16-head blocks (workgroups per sequence and split)
     int nsplit;
@@ -1227,8 +1230,32 @@ smla_status device_check() {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+#endif  // SMLA_PAGED_TU
 
 }  // namespace
+
+// The paged-pool instances of the decode kernel are built in a translation
+// unit of their own (smla_paged.hip includes this file with SMLA_PAGED_TU):
+// the contiguous instances are compiled with MFMA results in VGPRs (the
+// logit accumulators then need no copy out of AGPRs, build.py), which makes
+// the paged instances, 15 registers fuller, spill into AGPRs.  This launcher
+// is their only entry.
+__attribute__((visibility("hidden"))) void smla_launch_paged_decode(const void* args, size_t bytes,
+                                                                    int row_format, unsigned grid,
+                                                                    hipStream_t hs);
+
+#ifdef SMLA_PAGED_TU
+void smla_launch_paged_decode(const void* args, size_t bytes, int row_format, unsigned grid, hipStream_t hs) {
+    DecodeArgs a;
+    if (bytes != sizeof(a)) return;   // both units see the same struct; never taken
+    memcpy(&a, args, sizeof(a));
+    const dim3 g(grid), blk(64 * kWaves);
+    if (row_format == SMLA_ROW_UE8M0_SCALES)
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, true>), g, blk, 0, hs, a);
+    else
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, true>), g, blk, 0, hs, a);
+}
+#else
 
 extern "C" {
 
@@ -1322,14 +1349,13 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     const dim3 g(grid), blk(64 * kWaves);
-    const bool paged = a.block_table != nullptr;
-    if (a.row_format == SMLA_ROW_UE8M0_SCALES) {
-        if (paged) hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, true>), g, blk, 0, hs, args);
-        else hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args);
-    } else {
-        if (paged) hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, true>), g, blk, 0, hs, args);
-        else hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args);
-    }
+    (void)hipGetLastError();   // a launch error reported below is this launch's
+    if (a.block_table != nullptr)
+        smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs);
+    else if (a.row_format == SMLA_ROW_UE8M0_SCALES)
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args);
+    else
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
@@ -1462,3 +1488,4 @@ int32_t smla_split_size(const smla_shape* shape) {
 }
 
 }  // extern "C"
+#endif  // SMLA_PAGED_TU
