@@ -97,6 +97,8 @@ def parse():
                     help="shared: the decode path; per-head: the per-head SIMT ablation kernel")
     ap.add_argument("--page-size", type=int, default=0,
                     help="0 = contiguous cache; else rows in a shuffled paged pool of this page size")
+    ap.add_argument("--page-order", default="shuffled", choices=("shuffled", "sequential"),
+                    help="pool pages in random order (default) or in sequence order")
     ap.add_argument("--row-format", type=int, default=0, choices=(0, 1),
                     help="cache rows: 0 = fp32 group scales (640 B), 1 = UE8M0 scale bytes (584 B)")
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto, > 768 MB)")
@@ -143,7 +145,8 @@ def main():
     b_i, j_i = np.nonzero(valid)
     paged = args.page_size > 0
     if paged:
-        lay = make_paged_layout(w, args.page_size, seed=args.config, spare_pages=64)
+        lay = make_paged_layout(w, args.page_size, seed=args.config, spare_pages=64,
+                                shuffle=args.page_order == "shuffled")
         flat = torch.from_numpy(physical_rows(w, lay)[b_i, j_i]).to(dev)
         cache_rows = lay.num_pages * lay.page_size
         log(f"paged pool: page size {lay.page_size}, {lay.num_pages} pages, table {lay.block_table.shape}")
@@ -322,7 +325,8 @@ def main():
                    "topk": K, "seq_len": int(w.kv_seq_stride), "kept_rows": n_rows,
                    "num_splits": ns, "split_size": chunk, "rotation": R,
                    "row_format": "ue8m0_scales_584B" if fmt == 1 else "fp32_scales_640B",
-                   "cache": f"paged, {args.page_size} rows per page" if paged else "contiguous per sequence",
+                   "cache": (f"paged, {args.page_size} rows per page, {args.page_order} pages" if paged
+                             else "contiguous per sequence"),
                    "kernel": "per-head SIMT ablation" if args.kernel == "per-head" else "shared-read MFMA",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -285,11 +285,12 @@ class PagedLayout:
 
 
 def make_paged_layout(w: Workload, page_size: int, *, seed: int = 0, spare_pages: int = 0,
-                      all_pages: bool = False) -> PagedLayout:
-    """Place the workload's rows in a shuffled pool.  A logical page gets a pool
-    page when a kept list entry falls in it (every page below the sequence
-    length with ``all_pages``); the others stay -1.  Pool pages are a random
-    permutation (seeded), plus ``spare_pages`` pages that no sequence uses."""
+                      all_pages: bool = False, shuffle: bool = True) -> PagedLayout:
+    """Place the workload's rows in a pool.  A logical page gets a pool page
+    when a kept list entry falls in it (every page below the sequence length
+    with ``all_pages``); the others stay -1.  Pool pages are a random
+    permutation (seeded), or in sequence order without ``shuffle``, plus
+    ``spare_pages`` pages that no sequence uses."""
     rng = np.random.Generator(np.random.PCG64(seed + 7919))
     pps = max(1, -(-int(w.seqlens.max() if w.batch else 1) // page_size))
     need = np.zeros((w.batch, pps), dtype=bool)
@@ -300,7 +301,7 @@ def make_paged_layout(w: Workload, page_size: int, *, seed: int = 0, spare_pages
     need[b_i, w.idx[b_i, j_i] // page_size] = True
     n_used = int(need.sum())
     num_pages = n_used + spare_pages
-    perm = rng.permutation(num_pages).astype(np.int32)
+    perm = (rng.permutation(num_pages) if shuffle else np.arange(num_pages)).astype(np.int32)
     bt = np.full((w.batch, pps), -1, dtype=np.int32)
     bt[need] = perm[:n_used]
     return PagedLayout(page_size=int(page_size), num_pages=int(num_pages), block_table=bt)
