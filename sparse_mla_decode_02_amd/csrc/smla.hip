@@ -1239,21 +1239,23 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 // the contiguous instances are compiled with MFMA results in VGPRs (the
 // logit accumulators then need no copy out of AGPRs, build.py), which makes
 // the paged instances, 15 registers fuller, spill into AGPRs.  This launcher
-// is their only entry.
-__attribute__((visibility("hidden"))) void smla_launch_paged_decode(const void* args, size_t bytes,
+// is their only entry; it returns false without launching when the two units
+// disagree on the argument block.
+__attribute__((visibility("hidden"))) bool smla_launch_paged_decode(const void* args, size_t bytes,
                                                                     int row_format, unsigned grid,
                                                                     hipStream_t hs);
 
 #ifdef SMLA_PAGED_TU
-void smla_launch_paged_decode(const void* args, size_t bytes, int row_format, unsigned grid, hipStream_t hs) {
+bool smla_launch_paged_decode(const void* args, size_t bytes, int row_format, unsigned grid, hipStream_t hs) {
     DecodeArgs a;
-    if (bytes != sizeof(a)) return;   // both units see the same struct; never taken
+    if (bytes != sizeof(a)) return false;
     memcpy(&a, args, sizeof(a));
     const dim3 g(grid), blk(64 * kWaves);
     if (row_format == SMLA_ROW_UE8M0_SCALES)
         hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, true>), g, blk, 0, hs, a);
     else
         hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, true>), g, blk, 0, hs, a);
+    return true;
 }
 #else
 
@@ -1350,9 +1352,9 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     const dim3 g(grid), blk(64 * kWaves);
     (void)hipGetLastError();   // a launch error reported below is this launch's
-    if (a.block_table != nullptr)
-        smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs);
-    else if (a.row_format == SMLA_ROW_UE8M0_SCALES)
+    if (a.block_table != nullptr) {
+        if (!smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs)) return SMLA_ERR_HIP;
+    } else if (a.row_format == SMLA_ROW_UE8M0_SCALES)
         hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args);
     else
         hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args);
