@@ -237,6 +237,43 @@ smla_status sparse_mla_combine(const float* o_part, const float* lse_part, int32
 /* Static description of a status code. */
 const char* smla_status_str(smla_status status);
 
+/*
+ * Environment overrides, read once when the library is loaded:
+ *
+ *   SMLA_NSPLIT=n          the split count used when a shape leaves it to the
+ *                          library (num_splits == 0), 1 <= n <= 4096; clamped
+ *                          to the number of 32-token tiles like an explicit
+ *                          request.  smla_num_splits and smla_workspace_bytes
+ *                          follow it.  Other values are ignored.
+ *   SMLA_DEBUG_VALIDATE=1  (any value other than "" and "0") every decode call
+ *                          first launches, on the same stream, a scan of its
+ *                          device-resident inputs (seqlens, topk_idx and the
+ *                          block table), which the library otherwise never
+ *                          inspects.  Conditions found are OR-ed into a
+ *                          per-device word that smla_debug_flags reads.  The
+ *                          decode results do not change; the scan costs
+ *                          O(batch * topk^2) comparisons, so it is for debugging.
+ *
+ * The 16-head block and the four waves per workgroup are fixed by the kernel's
+ * matrix-instruction shape and are not configurable.
+ */
+#define SMLA_DBG_SEQLEN    1u  /* a seqlens[b] < 0 or above the rows a sequence can address
+                                  (kv_seq_stride; pages_per_seq * page_size when paged) */
+#define SMLA_DBG_INDEX     2u  /* an entry < -1 or >= seqlens[b] (skipped) */
+#define SMLA_DBG_PAGE      4u  /* paged: an entry below seqlens[b] whose block-table slot is
+                                  < 0 or >= num_pages (skipped) */
+#define SMLA_DBG_DUPLICATE 8u  /* a list holds the same kept entry twice (counted twice) */
+
+/* 1 when SMLA_DEBUG_VALIDATE was set at load, else 0. */
+int32_t smla_debug_validate_enabled(void);
+
+/* Waits for the current device to finish (hipDeviceSynchronize), stores in
+ * *flags the SMLA_DBG_* bits found by the scans run on it since the library
+ * was loaded or the word was last cleared, and clears the word when clear is
+ * non-zero.  0 when no scan ran.  Not for use under stream capture.
+ * Errors: SMLA_ERR_NULL, SMLA_ERR_NO_DEVICE, SMLA_ERR_UNSUPPORTED, SMLA_ERR_HIP. */
+smla_status smla_debug_flags(uint32_t* flags, int32_t clear);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,11 @@ STATUS_NAMES = {
 
 EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine",
            "sparse_mla_decode_paged", "sparse_mla_decode_partials_paged", "sparse_mla_decode_per_head",
-           "smla_workspace_bytes", "smla_num_splits", "smla_split_size", "smla_status_str")
+           "smla_workspace_bytes", "smla_num_splits", "smla_split_size", "smla_status_str",
+           "smla_debug_validate_enabled", "smla_debug_flags")
+
+# condition bits of the SMLA_DEBUG_VALIDATE input scan (smla.h)
+DBG_SEQLEN, DBG_INDEX, DBG_PAGE, DBG_DUPLICATE = 1, 2, 4, 8
 
 
 class SmlaShape(ctypes.Structure):
@@ -84,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_decode_paged.restype = ctypes.c_int
         L.sparse_mla_decode_partials_paged.argtypes = [vp, vp, vp, vp, vp, f32, shp, pgd, vp, vp, vp]
         L.sparse_mla_decode_partials_paged.restype = ctypes.c_int
+        L.smla_debug_validate_enabled.argtypes = []
+        L.smla_debug_validate_enabled.restype = i32
+        L.smla_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
+        L.smla_debug_flags.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -95,6 +103,19 @@ def status_str(status: int) -> str:
 def _check(status: int):
     if status != SMLA_OK:
         raise SmlaError(status, status_str(status))
+
+
+def debug_validate_enabled() -> bool:
+    """True when SMLA_DEBUG_VALIDATE was set when the library was loaded."""
+    return bool(lib().smla_debug_validate_enabled())
+
+
+def debug_flags(clear: bool = False) -> int:
+    """SMLA_DBG_* bits found by the input scans on the current device since the
+    load or the last clear; synchronizes the device."""
+    v = ctypes.c_uint32(0)
+    _check(lib().smla_debug_flags(ctypes.byref(v), 1 if clear else 0))
+    return v.value
 
 
 def make_shape(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> SmlaShape:

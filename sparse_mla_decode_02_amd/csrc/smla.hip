@@ -51,6 +51,7 @@
 //    absolute on outputs near 4 once the bf16 output rounding is added.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <type_traits>
@@ -723,6 +724,57 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
     if (row >= rows) return;
     combine_row(o_part, lse_part, row, nsplit, out, lse, threadIdx.x & 63);
 }
+
+// Debug scan of the device-resident inputs, launched ahead of the decode
+// kernel when SMLA_DEBUG_VALIDATE is set: the conditions it finds (SMLA_DBG_*)
+// are OR-ed into g_debug_flags, which smla_debug_flags reads.  The results of
+// the decode do not depend on it.
+__device__ uint32_t g_debug_flags;
+
+struct ValidateArgs {
+    const int32_t* idx;
+    const int32_t* seqlens;
+    const int32_t* block_table;   // NULL for a contiguous cache
+    int64_t reach;                // rows a sequence can address: kv_seq_stride, or pages_per_seq << page_shift
+    int32_t topk, page_shift, pages_per_seq;
+    uint32_t num_pages;
+};
+
+// One workgroup per sequence.  Repeated entries are found by comparing every
+// kept entry with the later ones, 1024 at a time staged in LDS: O(topk^2) per
+// list, which is why this is a debug path.
+__global__ __launch_bounds__(256) void smla_validate_kernel(ValidateArgs a) {
+    __shared__ int32_t part[1024];
+    const int b = blockIdx.x;
+    const int32_t* row = a.idx + (int64_t)b * a.topk;
+    const int32_t sl = a.seqlens[b];
+    const int64_t kept_below = sl < 0 ? 0 : (sl < a.reach ? (int64_t)sl : a.reach);
+    uint32_t f = (threadIdx.x == 0 && (sl < 0 || (int64_t)sl > a.reach)) ? SMLA_DBG_SEQLEN : 0u;
+    for (int j = threadIdx.x; j < a.topk; j += blockDim.x) {
+        const int32_t e = row[j];
+        if (e < -1 || (e >= 0 && e >= sl)) f |= SMLA_DBG_INDEX;
+        if (a.block_table != nullptr && e >= 0 && e < kept_below) {
+            const int32_t pg = a.block_table[(int64_t)b * a.pages_per_seq + (e >> a.page_shift)];
+            if (pg < 0 || (uint32_t)pg >= a.num_pages) f |= SMLA_DBG_PAGE;
+        }
+    }
+    for (int c0 = 0; c0 < a.topk; c0 += 1024) {
+        const int n = min(1024, a.topk - c0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += blockDim.x) part[i] = row[c0 + i];
+        __syncthreads();
+        for (int j = threadIdx.x; j < c0 + n; j += blockDim.x) {
+            const int32_t e = row[j];
+            if (e < 0 || e >= kept_below) continue;
+            for (int i = max(j + 1 - c0, 0); i < n; i++)
+                if (part[i] == e) {
+                    f |= SMLA_DBG_DUPLICATE;
+                    break;
+                }
+        }
+    }
+    if (f != 0u) atomicOr(&g_debug_flags, f);
+}
 #endif
 
 // Paged pool: the page ids of a tile's entries, 32 per wave and slot, after
@@ -1155,6 +1207,28 @@ int log2_exact(int32_t v) {
 constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
 constexpr int kMaxSplits = 4096;     // bound on the split count
 
+// Environment overrides, read once when the library is loaded:
+//   SMLA_NSPLIT=n           split count used when a shape leaves it to the
+//                           library (num_splits == 0), 1 <= n <= kMaxSplits
+//   SMLA_DEBUG_VALIDATE=1   scan the device-resident inputs before every decode
+struct EnvConfig {
+    int nsplit;           // 0: the heuristic
+    int debug_validate;
+};
+
+EnvConfig read_env() {
+    EnvConfig c = {0, 0};
+    if (const char* v = getenv("SMLA_NSPLIT")) {
+        char* end = nullptr;
+        const long n = strtol(v, &end, 10);
+        if (end != v && *end == '\0' && n >= 1 && n <= kMaxSplits) c.nsplit = (int)n;
+    }
+    if (const char* v = getenv("SMLA_DEBUG_VALIDATE")) c.debug_validate = (v[0] != '\0' && strcmp(v, "0") != 0);
+    return c;
+}
+
+const EnvConfig g_env = read_env();
+
 // Split count when the caller leaves it to the library.  A workgroup's time is
 // taken as (tiles per wave + 1) tile times, a launch as that times the number
 // of rounds of kComputeUnits workgroups, and any split adds one tile time for
@@ -1181,7 +1255,7 @@ Plan make_plan(const smla_shape* s) {
     p.n_hb = s->num_heads / 16;
     const int tiles = (s->topk + kTile - 1) / kTile;
     int ns = s->num_splits;
-    if (ns == 0) ns = choose_splits(s->batch * p.n_hb, tiles);
+    if (ns == 0) ns = g_env.nsplit > 0 ? g_env.nsplit : choose_splits(s->batch * p.n_hb, tiles);
     if (ns > tiles) ns = tiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
@@ -1346,12 +1420,28 @@ static smla_status prepare(const void* q, const void* kv_cache, const int32_t* t
     return SMLA_OK;
 }
 
+// Under SMLA_DEBUG_VALIDATE: the input scan, on the stream of the decode.
+static bool launch_validate(const DecodeArgs& a, hipStream_t hs) {
+    ValidateArgs v;
+    v.idx = a.idx;
+    v.seqlens = a.seqlens;
+    v.block_table = a.block_table;
+    v.reach = a.pages_per_seq > 0 ? ((int64_t)a.pages_per_seq << a.page_shift) : a.kv_seq_stride;   // paged : contiguous
+    v.topk = a.topk;
+    v.page_shift = a.page_shift;
+    v.pages_per_seq = a.pages_per_seq;
+    v.num_pages = a.pool_rows >> a.page_shift;
+    hipLaunchKernelGGL(smla_validate_kernel, dim3(a.batch), dim3(256), 0, hs, v);
+    return hipGetLastError() == hipSuccess;
+}
+
 static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const int grid = a.batch * p.n_hb * p.nsplit;
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     const dim3 g(grid), blk(64 * kWaves);
     (void)hipGetLastError();   // a launch error reported below is this launch's
+    if (g_env.debug_validate && !launch_validate(a, hs)) return SMLA_ERR_HIP;
     if (a.block_table != nullptr) {
         if (!smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs)) return SMLA_ERR_HIP;
     } else if (a.row_format == SMLA_ROW_UE8M0_SCALES)
@@ -1477,6 +1567,8 @@ smla_status sparse_mla_decode_per_head(const void* q, const void* kv_cache, cons
     a.topk = shape->topk;
     const int rows = shape->batch * shape->num_heads;
     const dim3 g((rows + 3) / 4), blk(256);
+    (void)hipGetLastError();
+    if (g_env.debug_validate && !launch_validate(d, (hipStream_t)stream)) return SMLA_ERR_HIP;
     if (shape->row_format == SMLA_ROW_UE8M0_SCALES)
         hipLaunchKernelGGL(smla_per_head_kernel<SMLA_ROW_UE8M0_SCALES>, g, blk, 0, (hipStream_t)stream, a);
     else
@@ -1487,6 +1579,26 @@ smla_status sparse_mla_decode_per_head(const void* q, const void* kv_cache, cons
 int32_t smla_split_size(const smla_shape* shape) {
     if (!shape_ok(shape)) return -1;
     return make_plan(shape).chunk;
+}
+
+int32_t smla_debug_validate_enabled(void) { return g_env.debug_validate; }
+
+smla_status smla_debug_flags(uint32_t* flags, int32_t clear) {
+    if (!flags) return SMLA_ERR_NULL;
+    smla_status st = device_check();
+    if (st != SMLA_OK) return st;
+    if (hipDeviceSynchronize() != hipSuccess) return SMLA_ERR_HIP;
+    uint32_t v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_flags), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return SMLA_ERR_HIP;
+    if (clear) {
+        const uint32_t zero = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) !=
+            hipSuccess)
+            return SMLA_ERR_HIP;
+    }
+    *flags = v;
+    return SMLA_OK;
 }
 
 }  // extern "C"
