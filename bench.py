@@ -147,7 +147,9 @@ def main():
     if paged:
         lay = make_paged_layout(w, args.page_size, seed=args.config, spare_pages=64,
                                 shuffle=args.page_order == "shuffled")
-        flat = torch.from_numpy(physical_rows(w, lay)[b_i, j_i]).to(dev)
+        phys = physical_rows(w, lay)[b_i, j_i]
+        assert (phys >= 0).all() and phys.max(initial=-1) < lay.num_pages * lay.page_size
+        flat = torch.from_numpy(phys).to(dev)
         cache_rows = lay.num_pages * lay.page_size
         log(f"paged pool: page size {lay.page_size}, {lay.num_pages} pages, table {lay.block_table.shape}")
     else:

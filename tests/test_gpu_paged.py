@@ -28,7 +28,8 @@ def device_paged_inputs(w, lay):
     q = torch.from_numpy(w.q_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
     pool = torch.full((lay.num_pages * lay.page_size, w.row_bytes), 0xFF, dtype=torch.uint8, device=DEV)
     phys = physical_rows(w, lay)
-    b_i, j_i = np.nonzero(w.valid)
+    b_i, j_i = np.nonzero(phys >= 0)    # rows that a page of the pool holds
+    assert phys.max(initial=-1) < lay.num_pages * lay.page_size
     if len(b_i):
         pool[torch.from_numpy(phys[b_i, j_i]).to(DEV)] = torch.from_numpy(
             np.ascontiguousarray(w.rows[b_i, j_i])).to(DEV)

@@ -308,18 +308,23 @@ def make_paged_layout(w: Workload, page_size: int, *, seed: int = 0, spare_pages
 
 
 def physical_rows(w: Workload, layout: PagedLayout) -> np.ndarray:
-    """Pool row of every list entry (-1 for an entry that is not kept)."""
+    """Pool row of every list entry: -1 for an entry that is not kept, or whose
+    position lies past its block-table row, or whose page id is outside the
+    pool (such an entry reaches no row; it is masked)."""
     ps = layout.page_size
     t = np.where(w.valid, w.idx, 0).astype(np.int64)
     b = np.arange(w.batch)[:, None]
-    page = layout.block_table[b, t // ps].astype(np.int64)
-    return np.where(w.valid, page * ps + t % ps, -1)
+    p = t // ps
+    in_table = p < layout.pages_per_seq
+    page = layout.block_table[b, np.minimum(p, layout.pages_per_seq - 1)].astype(np.int64)
+    ok = w.valid & in_table & (page >= 0) & (page < layout.num_pages)
+    return np.where(ok, page * ps + t % ps, -1)
 
 
 def build_host_pool(w: Workload, layout: PagedLayout) -> np.ndarray:
     """The pool uint8 [num_pages * page_size, row bytes]: kept rows placed, rest 0xFF."""
     pool = np.full((layout.num_pages * layout.page_size, w.row_bytes), 0xFF, dtype=np.uint8)
     phys = physical_rows(w, layout)
-    b_i, j_i = np.nonzero(w.valid)
+    b_i, j_i = np.nonzero(phys >= 0)
     pool[phys[b_i, j_i]] = w.rows[b_i, j_i]
     return pool
