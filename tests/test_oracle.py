@@ -390,3 +390,31 @@ def test_entries_past_the_stride_are_skipped():
     ref, rlse, _ = oracle.decode_raw(w.q_bits, cache, 200, ref_idx, w.seqlens, w.heads, w.scale)
     assert np.array_equal(out.view(np.uint64), ref.view(np.uint64))
     assert np.array_equal(lse.view(np.uint64), rlse.view(np.uint64))
+
+
+def test_pool_builder_places_only_rows_a_page_holds():
+    # entries whose block-table page is unset, negative or past the pool reach
+    # no pool row: physical_rows gives -1 for them, the pool builder places the
+    # other rows and never indexes outside the pool, and the oracle over that
+    # pool equals the oracle with those entries replaced by -1
+    from workloads import physical_rows
+    w = make_workload(seed=47, batch=3, heads=16, topk=80, seqlen=600)
+    lay = make_paged_layout(w, 32, seed=5, spare_pages=2)
+    t0 = [int(w.idx[b, 0]) // 32 for b in range(3)]
+    lay.block_table[0, t0[0]] = -1
+    lay.block_table[1, t0[1]] = -7
+    lay.block_table[2, t0[2]] = lay.num_pages + 2
+    phys = physical_rows(w, lay)
+    pg = np.where(w.idx >= 0, w.idx, 0) // 32
+    cut = np.stack([w.valid[b] & (pg[b] == t0[b]) for b in range(3)])
+    assert cut.sum() >= 3
+    assert (phys[cut] == -1).all()
+    assert (phys[w.valid & ~cut] >= 0).all()
+    assert phys.max() < lay.num_pages * lay.page_size
+    pool = build_host_pool(w, lay)
+    out, lse = oracle.decode_paged(w, lay, pool)
+    idx2 = np.where(cut, -1, w.idx).astype(np.int32)
+    ref, rlse, _ = oracle.decode_paged_raw(w.q_bits, pool, lay.num_pages, 32, lay.block_table, idx2,
+                                           w.seqlens, w.heads, w.scale)
+    assert np.array_equal(out.view(np.uint64), ref.view(np.uint64))
+    assert np.array_equal(lse.view(np.uint64), rlse.view(np.uint64))
