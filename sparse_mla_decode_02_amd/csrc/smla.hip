@@ -1229,10 +1229,16 @@ EnvConfig read_env() {
 
 const EnvConfig g_env = read_env();
 
-// Split count when the caller leaves it to the library.  A workgroup's time is
-// taken as (tiles per wave + 1) tile times, a launch as that times the number
-// of rounds of kComputeUnits workgroups, and any split adds one tile time for
-// the partials and the combine.  Ties go to fewer splits.
+// Split count when the caller leaves it to the library, from a cost model in
+// fortieths of a tile time fitted to measured steps (MI355X; 16- and 64-head
+// workloads of 1 to 96 sequences, 64 to 2048 entries, split counts 1 to 16):
+// a workgroup costs its tiles per wave plus 3 tile times of fixed cost (its
+// start, first entries and gather, and the merge) plus an eighth of a tile
+// time per tile it holds (its waves share the compute unit's gather and LDS
+// paths); a launch costs that times the number of rounds of kComputeUnits
+// workgroups; a split list adds one tile time for the partials and the
+// combine plus a fifth per four splits the combine merges.  Ties go to fewer
+// splits.
 int choose_splits(int base, int tiles) {
     if (base <= 0 || tiles <= 1) return 1;
     int best = 1;
@@ -1241,7 +1247,8 @@ int choose_splits(int base, int tiles) {
         const int per_block = (tiles + ns - 1) / ns;
         if (ns > 1 && (tiles + per_block - 1) / per_block < ns) continue;   // same chunks as fewer splits
         const long rounds = ((long)base * ns + kComputeUnits - 1) / kComputeUnits;
-        const long cost = rounds * ((per_block + kWaves - 1) / kWaves + 1) + (ns > 1 ? 1 : 0);
+        const long block = 40L * ((per_block + kWaves - 1) / kWaves + 3) + 5L * per_block;
+        const long cost = rounds * block + (ns > 1 ? 40L + 8L * ((ns + 3) / 4) : 0L);
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
             best = ns;
