@@ -59,6 +59,12 @@ def test_split_resolution_and_workspace_size():
         n = smla.num_splits(B, H, k)
         assert n >= 1
         assert n <= max(1, -(-k // 32))
+    # the model's picks on the five benchmark workloads (the fastest measured
+    # split counts on MI355X): 1, 8, 2, 2, 1
+    picks = [smla.num_splits(B, H, k, 0, S) for B, H, k, S in
+             [(1, 16, 64, 256), (4, 16, 512, 8192), (32, 64, 512, 32768), (96, 16, 2048, 65536),
+              (64, 64, 2048, 131072)]]
+    assert picks == [1, 8, 2, 2, 1]
     # invalid shapes
     assert smla.num_splits(1, 15, 64) == -1
     assert smla.num_splits(1, 16, -1) == -1
