@@ -544,6 +544,38 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
 
     issue_part(std::integral_constant<int, 1>{});
 
+    // ---------------- O^T += V^T . P^T: operand addresses, first groups' reads
+    // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2),
+    // byte half j%2; rope V^T via tr16, lane 16q + 4r + c supplies
+    // slot_token(8q + r), then slot_token(8q + 4 + r), columns 4c..4c+3 of each
+    // 16-column block.  The reads of group g + 1 are issued before group g is
+    // converted (one wave per SIMD has no other wave to hide LDS latency),
+    // and the first two groups' reads before the softmax, whose cross-lane
+    // reductions and exponentials then cover their latency.
+    // value pieces 4g + cb of this lane's token: piece cb plus 2048 g bytes
+    const int vpos = lds_pos(slot_token(8 * qg + (ln >> 1)));
+    const lds_u8* tr_cb[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) tr_cb[cb] = st + piece_addr(cb, vpos, ln & 1);
+    // rope bytes 32 dt + 8 (ln & 3): piece 28 + 2 dt + ((ln & 3) >> 1), half
+    // ln & 1; dt and dt + 2 are 2048 bytes apart
+    const int rpos0 = lds_pos(slot_token(8 * qg + (ln >> 2)));
+    const int rpos1 = lds_pos(slot_token(8 * qg + 4 + (ln >> 2)));
+    const int rp = kCodePieces + ((ln & 3) >> 1);
+    const lds_u8* r0[2] = {st + piece_addr(rp, rpos0, ln & 1), st + piece_addr(rp + 2, rpos0, ln & 1)};
+    const lds_u8* r1[2] = {st + piece_addr(rp, rpos1, ln & 1), st + piece_addr(rp + 2, rpos1, ln & 1)};
+    i32x2 vraw[2][4];
+    f32x4 svv[2][2];
+    auto load_group = [&](int g, int buf) {
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++)
+            vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_cb[cb] + 2048 * g));
+        svv[buf][0] = *(lds_cf32x4*)(sT + g * kTile + lds_pos(4 * qg));
+        svv[buf][1] = *(lds_cf32x4*)(sT + g * kTile + lds_pos(16 + 4 * qg));
+    };
+    load_group(0, 0);
+    load_group(1, 1);
+
     // ---------------- online softmax (log2 domain), lazy rescale
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -574,39 +606,12 @@ __device__ __forceinline__ void compute_tile(const lds_u8* st, uint64_t vmask, c
 
     issue_part(std::integral_constant<int, 2>{});
 
-    // ---------------- O^T += V^T . P^T
-    // V^T operands: tr8 source rows, lane 16q + j supplies token slot_token(8q + j/2),
-    // byte half j%2; rope V^T via tr16, lane 16q + 4r + c supplies
-    // slot_token(8q + r), then slot_token(8q + 4 + r), columns 4c..4c+3 of each
-    // 16-column block.  The reads of group g + 1 are issued before group g is
-    // converted (one wave per SIMD has no other wave to hide LDS latency).
-    // value pieces 4g + cb of this lane's token: piece cb plus 2048 g bytes
-    const int vpos = lds_pos(slot_token(8 * qg + (ln >> 1)));
-    const lds_u8* tr_cb[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; cb++) tr_cb[cb] = st + piece_addr(cb, vpos, ln & 1);
-    // rope bytes 32 dt + 8 (ln & 3): piece 28 + 2 dt + ((ln & 3) >> 1), half
-    // ln & 1; dt and dt + 2 are 2048 bytes apart
-    const int rpos0 = lds_pos(slot_token(8 * qg + (ln >> 2)));
-    const int rpos1 = lds_pos(slot_token(8 * qg + 4 + (ln >> 2)));
-    const int rp = kCodePieces + ((ln & 3) >> 1);
-    const lds_u8* r0[2] = {st + piece_addr(rp, rpos0, ln & 1), st + piece_addr(rp + 2, rpos0, ln & 1)};
-    const lds_u8* r1[2] = {st + piece_addr(rp, rpos1, ln & 1), st + piece_addr(rp + 2, rpos1, ln & 1)};
-    i32x2 vraw[2][4];
-    f32x4 svv[2][2];
-    auto load_group = [&](int g, int buf) {
-#pragma unroll
-        for (int cb = 0; cb < 4; cb++)
-            vraw[buf][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tr_cb[cb] + 2048 * g));
-        svv[buf][0] = *(lds_cf32x4*)(sT + g * kTile + lds_pos(4 * qg));
-        svv[buf][1] = *(lds_cf32x4*)(sT + g * kTile + lds_pos(16 + 4 * qg));
-    };
-    load_group(0, 0);
+    // ---------------- O^T += V^T . P^T, group by group
     s16x4 rv[4][2];
 #pragma unroll
     for (int g = 0; g < 7; g++) {
         const int cur = g & 1;
-        if (g + 1 < 7) load_group(g + 1, cur ^ 1);
+        if (g >= 1 && g + 1 < 7) load_group(g + 1, cur ^ 1);
         if (g == 1) {
 #pragma unroll
             for (int dt = 0; dt < 4; dt++) {
