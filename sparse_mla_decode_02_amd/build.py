@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
 # (64 instructions per tile).  Not for the paged instances (smla_paged.hip):
 # there it makes registers spill into AGPRs.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# The first kernel arguments in SGPRs at wave start (the decode kernel's ten
+# leading scalars, the combine kernel's six): no dependent kernel-argument load
+# before a kernel's first memory requests.
+PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=10"]
 
 
 def hipcc() -> str:
@@ -52,8 +56,8 @@ def build(verbose: bool = False, extra: list | None = None) -> str:
     try:
         obj_main = os.path.join(tmp_dir, "smla.o")
         obj_paged = os.path.join(tmp_dir, "smla_paged.o")
-        _run([hipcc(), *HIPCC_FLAGS, *VGPR_FORM, *(extra or []), "-c", SRC, "-o", obj_main], verbose)
-        _run([hipcc(), *HIPCC_FLAGS, *(extra or []), "-c", SRC_PAGED, "-o", obj_paged], verbose)
+        _run([hipcc(), *HIPCC_FLAGS, *VGPR_FORM, *PRELOAD, *(extra or []), "-c", SRC, "-o", obj_main], verbose)
+        _run([hipcc(), *HIPCC_FLAGS, *PRELOAD, *(extra or []), "-c", SRC_PAGED, "-o", obj_paged], verbose)
         tmp = LIB + ".tmp" + tag
         _run([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", obj_main, obj_paged, "-o", tmp], verbose)
         os.replace(tmp, LIB)

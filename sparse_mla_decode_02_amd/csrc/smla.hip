@@ -353,7 +353,7 @@ struct DecodeArgs {
     float logit_factor;   // scale * log2(e)
     int32_t batch, heads, topk, nsplit, chunk, n_hb;
     int32_t force_partials;   // write split partials even when nsplit == 1
-    int32_t xcd_remap;        // grid is a multiple of 8: keep a sequence's blocks on one XCD
+    int32_t xcd_remap;        // host only: grid is a multiple of 8, keep a sequence's blocks on one XCD
     int32_t row_format;       // host only: selects the kernel instance
     // paged pool (kv is the pool): block_table [batch][pages_per_seq]
     const int32_t* block_table;
@@ -794,8 +794,27 @@ static_assert(kPagedLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup"
 // their online-softmax states once, through LDS, and write the split's
 // normalised output and log-sum-exp (or the final bf16 result).
 // F: row format; P: rows in a paged pool found through the block table.
+// The values the first list entries and rows wait for come as leading scalar
+// arguments, which the build preloads into SGPRs (kernarg preload, gfx950):
+// no kernel-argument load before the first memory requests (~0.8 us per
+// launch at the default workload).  remap_stride is gridDim.x / 8 when the
+// XCD remap applies, else 0; the rest of DecodeArgs is read as usual.
 template <int F, bool P>
-__global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8_t* kv, const int32_t* idx,
+                                                                    const int32_t* seqlens, int64_t kv_seq_stride,
+                                                                    int32_t topk, int32_t nsplit, int32_t chunk,
+                                                                    int32_t n_hb, int32_t heads,
+                                                                    int32_t remap_stride, DecodeArgs a) {
+    a.kv = kv;
+    a.idx = idx;
+    a.seqlens = seqlens;
+    a.kv_seq_stride = kv_seq_stride;
+    a.seq_bytes = (uint32_t)kv_seq_stride * (uint32_t)RowFormat<F>::kBytes;
+    a.topk = topk;
+    a.nsplit = nsplit;
+    a.chunk = chunk;
+    a.n_hb = n_hb;
+    a.heads = heads;
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[P ? kPagedLdsBytes : kLdsBytes];
     lds_u8* const lds = (lds_u8*)lds_raw;
 
@@ -805,7 +824,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(DecodeArgs 
     const int ln = lane & 15;                  // head column of the 16x16 tiles
 
     int bid = blockIdx.x;
-    if (a.xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+    if (remap_stride) bid = (bid & 7) * remap_stride + (bid >> 3);
     const int split = bid % a.nsplit;
     bid /= a.nsplit;
     const int hb = bid % a.n_hb;
@@ -1338,9 +1357,13 @@ bool smla_launch_paged_decode(const void* args, size_t bytes, int row_format, un
     memcpy(&a, args, sizeof(a));
     const dim3 g(grid), blk(64 * kWaves);
     if (row_format == SMLA_ROW_UE8M0_SCALES)
-        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, true>), g, blk, 0, hs, a);
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, true>), g, blk, 0, hs, a.kv, a.idx, a.seqlens,
+                           a.kv_seq_stride, a.topk, a.nsplit, a.chunk, a.n_hb, a.heads,
+                           a.xcd_remap ? (int32_t)(grid / 8) : 0, a);
     else
-        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, true>), g, blk, 0, hs, a);
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, true>), g, blk, 0, hs, a.kv, a.idx, a.seqlens,
+                           a.kv_seq_stride, a.topk, a.nsplit, a.chunk, a.n_hb, a.heads,
+                           a.xcd_remap ? (int32_t)(grid / 8) : 0, a);
     return true;
 }
 #else
@@ -1457,9 +1480,13 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     if (a.block_table != nullptr) {
         if (!smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs)) return SMLA_ERR_HIP;
     } else if (a.row_format == SMLA_ROW_UE8M0_SCALES)
-        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args);
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args.kv, args.idx, args.seqlens,
+                           args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb, args.heads,
+                           args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
     else
-        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args);
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args.kv, args.idx, args.seqlens,
+                           args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb, args.heads,
+                           args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
