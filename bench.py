@@ -106,13 +106,58 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="no rotation (last-level-cache warm)")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="host only: time the fp64 oracle on every workload (all threads; one thread "
+                         "for workloads 1-3), median of 3 runs, and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (counter calibration)")
     return ap.parse_args()
 
 
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_table(args):
+    """The fp64 CPU oracle timed on every workload on this host: a reported
+    baseline, not a target.  All threads (OpenMP default) for workloads 1-5,
+    then one thread for workloads 1-3; each entry the median of 3 runs."""
+    import oracle
+    from workloads import build_host_cache, config_workload
+    rows = []
+    for threads, cfgs in ((0, (1, 2, 3, 4, 5)), (1, (1, 2, 3))):
+        for c in cfgs:
+            w = config_workload(c, row_format=args.row_format)
+            hc = build_host_cache(w)
+            times, used = [], 0
+            for _ in range(3):
+                t0 = time.perf_counter()
+                _, _, used = oracle.decode_raw(w.q_bits, hc, w.kv_seq_stride, w.idx, w.seqlens, w.heads, w.scale,
+                                               row_format=w.row_format, nthreads=threads)
+                times.append(time.perf_counter() - t0)
+            del hc
+            t = sorted(times)[1]
+            row = {"workload": w.name, "config_number": c, "threads": int(used), "median_s": t,
+                   "queries_heads_per_s": w.batch * w.heads / t,
+                   "kv_gbps": float(w.valid.sum()) * ROW_ALGO_BYTES[w.row_format] / t / 1e9}
+            rows.append(row)
+            log(f"oracle {w.name}: {used} threads, median {t * 1e3:.1f} ms, "
+                f"{row['queries_heads_per_s']:.3g} q*h/s")
+    print(json.dumps({"kind": "oracle timing", "cpu": cpu_model(), "nproc": os.cpu_count(),
+                      "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "rows": rows}))
+
+
 def main():
     args = parse()
+    if args.oracle_table:
+        oracle_table(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the decode path shards by heads or sequences "
