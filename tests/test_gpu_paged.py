@@ -150,3 +150,49 @@ def test_paged_pool_beyond_4gb():
                                             w.scale)
     out, lse = run_paged(w, lay, num_splits=0)
     compare(out, lse, ref_out, ref_lse, label="paged pool > 4 GiB")
+
+
+def test_paged_graph_replays_match_eager_and_oracle():
+    # a captured paged split launch (UE8M0 rows, decode and combine kernels):
+    # replays interleaved with eager calls on the same workspace give the eager
+    # bits, and the eager result matches the paged oracle
+    w = make_workload(seed=302, batch=8, heads=64, topk=512, seqlen=8192, row_format=1)
+    lay = make_paged_layout(w, 64, seed=7, spare_pages=5)
+    ref_out, ref_lse, _ = oracle.decode_paged_raw(w.q_bits, build_host_pool(w, lay), lay.num_pages, 64,
+                                                  lay.block_table, w.idx, w.seqlens, w.heads, w.scale,
+                                                  row_format=1)
+    q, pool, bt, idx, sl = device_paged_inputs(w, lay)
+    ns = 4
+    ws = torch.empty(smla.workspace_bytes(w.batch, w.heads, w.topk, ns, 1, 1), dtype=torch.uint8, device=DEV)
+
+    def call(out, lse):
+        smla.sparse_mla_decode_paged(q, pool, bt, idx, sl, w.scale, out, lse, page_size=64,
+                                     num_pages=lay.num_pages, num_splits=ns, workspace=ws, row_format=1)
+
+    out_e = torch.empty((w.batch, w.heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse_e = torch.empty((w.batch, w.heads), device=DEV)
+    call(out_e, lse_e)
+    torch.cuda.synchronize()
+    compare(out_e.float().cpu().numpy().astype(np.float64), lse_e.cpu().numpy().astype(np.float64),
+            ref_out, ref_lse, label="paged graph eager")
+    ref = (out_e.clone(), lse_e.clone())
+    out_g = torch.empty_like(out_e)
+    lse_g = torch.empty_like(lse_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(out_g, lse_g)
+    torch.cuda.synchronize()
+    for r in range(3):
+        log(f"case: paged graph replay {r}")
+        out_g.fill_(float("nan"))
+        lse_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref[0]) and torch.equal(lse_g, ref[1]), r
+        call(out_e, lse_e)          # an eager call on the same workspace in between
+        torch.cuda.synchronize()
+        assert torch.equal(out_e, ref[0]) and torch.equal(lse_e, ref[1]), r
