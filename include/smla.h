@@ -72,7 +72,9 @@ typedef enum {
     SMLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
     SMLA_ERR_HIP = 5,          /* a HIP runtime call or launch failed */
     SMLA_ERR_ALIGN = 6,        /* a pointer violates its alignment rule */
-    SMLA_ERR_NO_DEVICE = 7     /* no HIP device is available */
+    SMLA_ERR_NO_DEVICE = 7,    /* no HIP device is available */
+    SMLA_ERR_SCRATCH = 8       /* sparse_mla_decode_noalloc: the shape's split partials
+                                  exceed SMLA_NOALLOC_SCRATCH_BYTES */
 } smla_status;
 
 typedef struct {
@@ -214,6 +216,30 @@ smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool,
 smla_status sparse_mla_decode_per_head(const void* q, const void* kv_cache, const int32_t* topk_idx,
                                        const int32_t* seqlens, float scale, void* out, float* lse,
                                        const smla_shape* shape, void* stream);
+
+/*
+ * sparse_mla_decode_noalloc -- sparse_mla_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split partials go to a fixed scratch
+ * array that the library holds on each GPU (SMLA_NOALLOC_SCRATCH_BYTES, a
+ * device array in the library's code object, kept until the process ends)
+ * instead of a caller workspace.  The call itself allocates nothing.
+ *
+ *   arguments as for sparse_mla_decode, without workspace and workspace_bytes
+ *
+ * Returns SMLA_ERR_SCRATCH, before anything is launched, when
+ * smla_workspace_bytes(shape) exceeds SMLA_NOALLOC_SCRATCH_BYTES (the split
+ * partials are 2052 bytes per (sequence, head, split), so e.g. 32 sequences x
+ * 64 heads x 2 splits fit).  Every call on one GPU uses that GPU's single
+ * scratch array: calls that may run at the same time on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller.  The
+ * scratch needs no clearing: each call overwrites every partial it reads.
+ * Results are bitwise those of sparse_mla_decode with the same shape.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+smla_status sparse_mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                                      const int32_t* seqlens, float scale, void* out, float* lse,
+                                      const smla_shape* shape, void* stream);
 
 /* List entries per split (C above, a multiple of 32); -1 for an invalid shape. */
 int32_t smla_split_size(const smla_shape* shape);

@@ -27,9 +27,11 @@ ROPE = 64
 STATUS_NAMES = {
     0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_UNSUPPORTED",
     4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_HIP", 6: "SMLA_ERR_ALIGN", 7: "SMLA_ERR_NO_DEVICE",
+    8: "SMLA_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024   # SMLA_NOALLOC_SCRATCH_BYTES
 
-EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine",
+EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine", "sparse_mla_decode_noalloc",
            "sparse_mla_decode_paged", "sparse_mla_decode_partials_paged", "sparse_mla_decode_per_head",
            "smla_workspace_bytes", "smla_num_splits", "smla_split_size", "smla_status_str",
            "smla_debug_validate_enabled", "smla_debug_flags")
@@ -79,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.smla_status_str.restype = ctypes.c_char_p
         L.sparse_mla_decode.argtypes = [vp, vp, vp, vp, f32, vp, vp, shp, vp, ctypes.c_size_t, vp]
         L.sparse_mla_decode.restype = ctypes.c_int
+        L.sparse_mla_decode_noalloc.argtypes = [vp, vp, vp, vp, f32, vp, vp, shp, vp]
+        L.sparse_mla_decode_noalloc.restype = ctypes.c_int
         L.sparse_mla_combine.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.sparse_mla_combine.restype = ctypes.c_int
         L.sparse_mla_decode_per_head.argtypes = [vp, vp, vp, vp, f32, vp, vp, shp, vp]
@@ -181,6 +185,22 @@ def sparse_mla_decode(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, num_sp
     _check(L.sparse_mla_decode(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(seqlens),
                                ctypes.c_float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape),
                                _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream)))
+    return out, lse
+
+
+def sparse_mla_decode_noalloc(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, num_splits=0,
+                              kv_seq_stride=None, stream=None, row_format=0):
+    """sparse_mla_decode without a workspace: the split partials use the
+    library's fixed per-GPU scratch (SMLA_NOALLOC_SCRATCH_BYTES); nothing is
+    allocated.  Calls that overlap on one GPU race."""
+    B, H, _ = q.shape
+    topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    if kv_seq_stride is None:
+        kv_seq_stride = _seq_stride(kv_cache, B, row_format)
+    shape = make_shape(B, H, topk, num_splits, kv_seq_stride, row_format)
+    _check(lib().sparse_mla_decode_noalloc(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(seqlens),
+                                           ctypes.c_float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape),
+                                           _stream_handle(stream)))
     return out, lse
 
 

@@ -54,6 +54,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 
@@ -1335,6 +1336,33 @@ smla_status device_check() {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Fixed split-partial scratch of sparse_mla_decode_noalloc: a device array in
+// the code object, one copy per GPU, held until the process ends.  Host code
+// never passes its name to a kernel (that is a host-side stand-in, not a device
+// address): the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept here.
+static __device__ __align__(256) uint8_t scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (nullptr on failure).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 #endif  // SMLA_PAGED_TU
 
 }  // namespace
@@ -1390,6 +1418,7 @@ const char* smla_status_str(smla_status s) {
         case SMLA_ERR_HIP: return "HIP runtime error";
         case SMLA_ERR_ALIGN: return "pointer misaligned";
         case SMLA_ERR_NO_DEVICE: return "no HIP device";
+        case SMLA_ERR_SCRATCH: return "split partials exceed the fixed scratch of sparse_mla_decode_noalloc";
     }
     return "unknown status";
 }
@@ -1613,6 +1642,24 @@ smla_status sparse_mla_decode_per_head(const void* q, const void* kv_cache, cons
     else
         hipLaunchKernelGGL(smla_per_head_kernel<SMLA_ROW_FP32_SCALES>, g, blk, 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
+smla_status sparse_mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                                      const int32_t* seqlens, float scale, void* out, float* lse,
+                                      const smla_shape* shape, void* stream) {
+    if (!shape) return SMLA_ERR_NULL;
+    if (!shape_ok(shape)) return SMLA_ERR_SHAPE;
+    const size_t need = workspace_for(shape, make_plan(shape));
+    if (need > (size_t)SMLA_NOALLOC_SCRATCH_BYTES) return SMLA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        const smla_status st = device_check();
+        if (st != SMLA_OK) return st;
+        ws = scratch_for_current_device();
+        if (ws == nullptr) return SMLA_ERR_HIP;
+    }
+    return decode_impl(q, kv_cache, nullptr, topk_idx, seqlens, scale, out, lse, shape, nullptr, ws,
+                       (size_t)SMLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int32_t smla_split_size(const smla_shape* shape) {

@@ -33,7 +33,7 @@ def test_exports_every_declared_function():
 
 @needs_lib
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = smla.status_str(code)
         assert isinstance(s, str) and s
     assert smla.status_str(0) == "ok"
@@ -201,3 +201,29 @@ def test_per_head_argument_errors():
     assert call(good, out=None) == 1
     assert call(smla.make_shape(2, 20, 64, 0, 128)) == 2
     assert call(good, out=ctypes.c_void_p((1 << 20) + 8)) == 6
+
+
+@needs_lib
+def test_noalloc_argument_errors_before_any_device_work():
+    L = smla.lib()
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(shape, **over):
+        a = dict(q=fake, kv=fake, idx=fake, sl=fake, out=fake, lse=fake)
+        a.update(over)
+        return L.sparse_mla_decode_noalloc(a["q"], a["kv"], a["idx"], a["sl"], ctypes.c_float(0.05), a["out"],
+                                           a["lse"], ctypes.byref(shape) if shape is not None else None, None)
+    assert call(None) == 1                                            # NULL shape
+    assert call(smla.make_shape(2, 20, 64, 2, 128)) == 2              # H not a multiple of 16
+    # split partials beyond the fixed scratch: rejected before any device work
+    big = smla.make_shape(64, 256, 2048, 16, 4096)
+    assert L.smla_workspace_bytes(ctypes.byref(big)) > smla.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 8
+    assert "scratch" in smla.status_str(8)
+    # the largest split count that fits at 32 sequences x 64 heads
+    fits = smla.make_shape(32, 64, 512, 2, 32768)
+    assert 0 < L.smla_workspace_bytes(ctypes.byref(fits)) <= smla.NOALLOC_SCRATCH_BYTES
+    import torch
+    if not torch.cuda.is_available():
+        assert call(fits) == 7                                        # valid, but no device here
+        assert call(fits, out=None) in (1, 7)
