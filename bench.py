@@ -351,7 +351,7 @@ def main():
             reps += 1
         del hc
         cpu = {"value": B * H * reps / t_cpu, "unit": "queries·heads/s", "cores": int(used),
-               "kind": "oracle",
+               "kind": "oracle", "cpu": cpu_model(), "nproc": os.cpu_count(),
                "sample": f"{reps} full runs of the {w.name} workload ({B * H} query-heads each), "
                          f"{t_cpu:.1f} s, fp64 OpenMP over (b,h)"}
         log(f"cpu oracle: {cpu['value']:.3g} q*h/s on {used} threads ({reps} reps, {t_cpu:.1f}s)")

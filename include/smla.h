@@ -77,10 +77,15 @@ typedef enum {
                                   exceed SMLA_NOALLOC_SCRATCH_BYTES */
 } smla_status;
 
+/* Largest top-k list a call accepts (larger: SMLA_ERR_SHAPE).  The pages'
+ * lists are 64 to 2048 entries; the bound keeps every byte offset into a list
+ * and the split search far inside 32 bits. */
+#define SMLA_MAX_TOPK (1 << 20)
+
 typedef struct {
     int32_t batch;          /* B >= 0: query tokens, one per sequence */
     int32_t num_heads;      /* H >= 0, multiple of 16, <= 256: this GPU's heads */
-    int32_t topk;           /* >= 0: entries in each top-k list */
+    int32_t topk;           /* 0 .. SMLA_MAX_TOPK: entries in each top-k list */
     int32_t num_splits;     /* >= 0: split-K chunks per list; 0 = library's choice */
     int64_t kv_seq_stride;  /* >= 1: cache rows between sequence b and b + 1;
                                kv_seq_stride * row bytes must be below 2^31 */
@@ -128,10 +133,12 @@ size_t smla_workspace_bytes(const smla_shape* shape);
  *
  * Numerical contract: q . K is accumulated in fp32 from the exact bf16 query
  * and exact fp8/bf16 key values, with the group scales applied in fp32; the
- * softmax weights enter the value product in fp16 (value codes exact), so
- * group scales must be finite and below 256 (UE8M0 bytes at most 134) and
- * rope values below 65504 in magnitude.  NaN inputs propagate to the
- * affected outputs.
+ * softmax weights enter the value product in fp16 (value codes exact): a
+ * weight is p * scale with p <= 2^8, so group scales must be finite with
+ * magnitude at most 255 (UE8M0 bytes at most 134, i.e. 2^7), and rope values
+ * below 65504 in magnitude.  Scales below 2^-14 give subnormal fp16 weights
+ * (fewer significant bits, on values that small in absolute terms).  NaN
+ * inputs propagate to the affected outputs.
  */
 smla_status sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* topk_idx,
                               const int32_t* seqlens, float scale, void* out, float* lse,

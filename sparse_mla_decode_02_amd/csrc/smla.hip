@@ -1210,7 +1210,8 @@ int row_bytes_of(int32_t fmt) {
 // paged calls do not use the stride but check it the same way.)
 bool shape_ok(const smla_shape* s) {
     return s && row_bytes_of(s->row_format) > 0 && s->batch >= 0 && s->num_heads >= 0 &&
-           s->num_heads % 16 == 0 && s->num_heads <= 256 && s->topk >= 0 && s->num_splits >= 0 &&
+           s->num_heads % 16 == 0 && s->num_heads <= 256 && s->topk >= 0 && s->topk <= SMLA_MAX_TOPK &&
+           s->num_splits >= 0 &&
            s->kv_seq_stride >= 1 && s->kv_seq_stride <= (((int64_t)1 << 31) - 1) / row_bytes_of(s->row_format);
 }
 

@@ -92,6 +92,10 @@ def test_argument_errors_before_any_device_work():
     assert _call(L, smla.make_shape(2, 20, 64, 1, 128)) == 2      # H not a multiple of 16
     assert _call(L, smla.make_shape(2, 272, 64, 1, 128)) == 2     # H too large
     assert _call(L, smla.make_shape(2, 16, -3, 1, 128)) == 2      # negative topk
+    assert _call(L, smla.make_shape(2, 16, (1 << 20) + 1, 1, 128)) == 2   # topk above SMLA_MAX_TOPK
+    assert _call(L, smla.make_shape(2, 16, 2 ** 31 - 1, 0, 128)) == 2     # would wrap byte offsets
+    assert smla.num_splits(2, 16, (1 << 20) + 1) == -1
+    assert smla.num_splits(2, 16, 1 << 20) >= 1                           # the bound itself is valid
     assert _call(L, smla.make_shape(-1, 16, 64, 1, 128)) == 2     # negative batch
     assert _call(L, smla.make_shape(2, 16, 64, -2, 128)) == 2     # negative splits
     assert _call(L, smla.make_shape(2, 16, 64, 1, 0)) == 2        # stride < 1

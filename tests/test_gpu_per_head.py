@@ -36,7 +36,7 @@ def reference(w):
     return out, lse
 
 
-@pytest.mark.parametrize("cfg,row_format", [(1, 0), (2, 0), (3, 0), (3, 1), (4, 0)])
+@pytest.mark.parametrize("cfg,row_format", [(1, 0), (2, 0), (3, 0), (3, 1), (4, 0), (5, 0)])
 def test_per_head_config_parity(cfg, row_format):
     log(f"case: per-head config {cfg} row format {row_format}")
     w = config_workload(cfg, row_format=row_format)
