@@ -89,9 +89,12 @@ typedef __attribute__((address_space(3))) const f32x4 lds_cf32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) const float lds_cf32;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+typedef __attribute__((address_space(3))) const f32x2 lds_cf32x2;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef __attribute__((address_space(3))) const int32_t lds_ci32;
 typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 // LDS tile slot.  The 36 16-byte pieces of a row (0..27 the fp8 codes, 28..35
 // the rope) are stored in 18 blocks of 1 KB: block 2j + hh holds pieces
@@ -1049,6 +1052,502 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined decode kernel (contiguous cache): one workgroup = (sequence b,
+// block hb of 16 heads, split), eight waves in two roles, one of each per
+// SIMD.  The split's list is taken in batches of two 32-token tiles, which
+// move through a ring of four batch buffers in LDS.  In step s:
+//   - the logit waves (0..3) compute S^T for 16-token half (w & 1) of tile
+//     (w >> 1) of batch s against the 16 heads (the bf16 MFMA product of the
+//     four-wave kernel), mask it, take as its base the running maximum, or its
+//     own maximum when that exceeds the running one by more than kTau, and
+//     write its weights p = 2^(z - base) to a weight table and its base per
+//     head to a statistics row;
+//   - the value waves (4..7) accumulate O^T += V^T . P^T for batch s - 1 over
+//     their own output columns (value wave i: nope groups 2i, 2i + 1, or group
+//     6 and the rope for i = 3), each half's weights scaled by 2^(base - M)
+//     (almost always 1: that branch is skipped);
+//   - every wave issues its share of the gathers of batch s + 2 (and wave 0
+//     the copy of the list entries of batch s + 3);
+// and one barrier ends the step, after each wave has waited for its own
+// gathers of batch s + 1.  At the top of every step all eight waves form the
+// same new running maximum M from the four bases of batch s - 1.  The two
+// roles share each SIMD, so one role's memory waits and dependency stalls are
+// filled by the other's work; the weights, not accumulators, cross between
+// waves, and no wave's registers exceed the 256 that two waves per SIMD allow.
+// Every tile of every batch is gathered (list entries past the split or
+// masked read row -1, i.e. zeros), so no wave ever reads stale bytes and the
+// tile loops carry no branches.
+// LDS: four batch buffers of two tile slots (the slot layout above) and two
+// weight tables (batch parity), 160 KB.  Row 7 of each slot, which the gathers
+// never write, holds the list entries of the batch after next (slots 0..3, by
+// batch parity, copied from memory by the DMA path like the rows) and the
+// bases (slots 4..7).  Every asynchronous memory read of the loop is such a
+// DMA into LDS, so each wave's waits count only its own DMAs.  At the start
+// the fourth buffer stages the workgroup's query (16 rows of 1 KB, read once
+// from memory instead of once per wave).
+constexpr int kV3Waves = 8;
+constexpr int kV3Tiles = 2;                               // tiles per batch
+constexpr int kV3Ring = 4;                                // batch buffers
+constexpr int kV3Batch = kV3Tiles * kSlot;                // 38912 bytes per batch buffer
+constexpr int kV3PTable = kV3Ring * kV3Batch;             // weight tables offset
+constexpr int kV3PTile = 16 * kTile * 4;                  // one tile's weights: [16 heads][32 tokens] fp32
+constexpr int kV3LdsBytes = kV3PTable + 2 * kV3Tiles * kV3PTile;
+static_assert(kV3LdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+static_assert(16 * 1024 <= kScaleTable, "the staged query stays clear of its slot's scale table");
+static_assert(kV3Batch == 2 * kSlot, "slot k of the ring is slot k & 1 of buffer k >> 1");
+
+// Byte offset in a weight table of tokens 4c..4c+3 of head h in a tile:
+// 16-byte chunks XOR-swizzled by head so that the 16 heads read by one
+// quarter-wave fall in distinct banks.
+__device__ __forceinline__ int ptable_chunk(int h, int c) { return 128 * h + 16 * (c ^ ((h >> 1) & 7)); }
+
+// Staged query: byte offset of 16-byte chunk c (columns 8c..8c+7) of head h,
+// chunks XOR-swizzled by h so that 16 heads read at one column fall in
+// distinct banks.
+__device__ __forceinline__ int qstage_addr(int h, int c) { return 1024 * h + 16 * (c ^ (h & 15)); }
+
+// fp16 weights fp16(p * s) of eight tokens (p0, p1 and s0, s1 hold tokens
+// 0..3 and 4..7): the fp32 product, rounded to fp16 (v_cvt_pk_f16_f32, round
+// to nearest even).  Plain arithmetic, not inline assembly, so that the
+// compiler sees these vector writes and keeps the wait states the matrix
+// instructions reading them require.
+__device__ __forceinline__ f16x8 weights_f16(f32x4 p0, f32x4 p1, f32x4 s0, f32x4 s1) {
+    const f32x4 w0 = p0 * s0, w1 = p1 * s1;
+    return f16x8{(_Float16)w0[0], (_Float16)w0[1], (_Float16)w0[2], (_Float16)w0[3],
+                 (_Float16)w1[0], (_Float16)w1[1], (_Float16)w1[2], (_Float16)w1[3]};
+}
+
+// Gathers issued per step by the wave of part i (0..3) of a tile: part 0 the
+// scale table and row blocks 0..3, part 1 blocks 4..7, part 2 blocks 8..11,
+// part 3 blocks 12..17 (block pairs j = 2i, 2i + 1, and j = 8 for part 3).
+template <int F>
+__device__ __forceinline__ constexpr int v3_gathers(int part) {
+    return part == 0 ? (F == SMLA_ROW_UE8M0_SCALES ? 1 : kScaleGathers) + 4 : part == 3 ? 6 : 4;
+}
+
+template <int F>
+__global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uint8_t* kv, const int32_t* idx,
+                                                                      const int32_t* seqlens, int64_t kv_seq_stride,
+                                                                      int32_t topk, int32_t nsplit, int32_t chunk,
+                                                                      int32_t n_hb, int32_t heads,
+                                                                      int32_t remap_stride, DecodeArgs a) {
+    a.kv = kv;
+    a.idx = idx;
+    a.seqlens = seqlens;
+    a.kv_seq_stride = kv_seq_stride;
+    a.seq_bytes = (uint32_t)kv_seq_stride * (uint32_t)RowFormat<F>::kBytes;
+    a.topk = topk;
+    a.nsplit = nsplit;
+    a.chunk = chunk;
+    a.n_hb = n_hb;
+    a.heads = heads;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kV3LdsBytes];
+    lds_u8* const lds = (lds_u8*)lds_raw;
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qg = lane >> 4;                  // lane group 0..3
+    const int ln = lane & 15;                  // head column of the 16x16 tiles
+
+    int bid = blockIdx.x;
+    if (remap_stride) bid = (bid & 7) * remap_stride + (bid >> 3);
+    const int split = bid % a.nsplit;
+    bid /= a.nsplit;
+    const int hb = bid % a.n_hb;
+    const int b = bid / a.n_hb;
+
+    const int head = 16 * hb + ln;
+    const int t_begin = split * a.chunk;
+    const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
+    const int nb = (n_ent + kV3Tiles * kTile - 1) / (kV3Tiles * kTile);
+    const int seqlen = (int)min((int64_t)a.seqlens[b], a.kv_seq_stride);
+    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
+    const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
+
+    // In the loop, logit wave w issues the gathers of tile w & 1 of each batch:
+    // half 0 (waves 0, 1) the scale table and block pairs 0..3, half 1 pairs
+    // 4..8.  In the prologue all eight waves gather batches 0 and 1: wave w
+    // part w >> 1 of tile w & 1 (part 0 the scale table and pairs 0, 1, part 1
+    // pairs 2, 3, part 2 pairs 4, 5, part 3 pairs 6..8).
+    const int gtile = wave & 1;
+    const int ghalf = (wave >> 1) & 1;
+    const int ppart = wave >> 1;
+    constexpr int kScaleInstr = F == SMLA_ROW_UE8M0_SCALES ? 1 : kScaleGathers;
+
+    // sanitised list entry of batch bt for lane l: tile l >> 5, position l & 31
+    // (row -1 past the split, past the sequence or masked)
+    auto sanitise = [&](int bt, int v) -> int {
+        return bt * (kV3Tiles * kTile) + lane < n_ent && v >= 0 && v < seqlen ? v : -1;
+    };
+    // the entries of batch bt in row 7 of slots 2 (bt & 1) and 2 (bt & 1) + 1:
+    // copied there by wave 0 (lanes past the split read zeros through the
+    // buffer range check), read back by the logit waves
+    const i32x4 irsrc = row_rsrc((const uint8_t*)idx_b, 4u * (uint32_t)n_ent);
+    auto stage_entries = [&](int bt) {
+        const uint32_t voff = 4u * (uint32_t)(bt * (kV3Tiles * kTile) + lane);
+        const uint32_t row7 = lds_addr + 2 * (bt & 1) * kSlot + kEntryTable;
+        if (lane < 32) gather4(voff, irsrc, row7);
+        else gather4(voff, irsrc, row7 + kSlot - 4 * 32);
+    };
+    auto read_entries = [&](int bt) -> int {
+        return sanitise(bt, ((lds_ci32*)(lds + (2 * (bt & 1) + (lane >> 5)) * kSlot + kEntryTable))[lane & 31]);
+    };
+    // bases of half j of the batch of parity p: row 7 of slot 4 + 2p + (j >> 1)
+    auto stats_row = [&](int parity, int j) -> lds_u8* {
+        return lds + (4 + 2 * parity + (j >> 1)) * kSlot + kEntryTable + 64 * (j & 1);
+    };
+    auto plan_batch = [&](int bt, int e) {
+        const int row = __builtin_amdgcn_ds_bpermute(4 * (32 * gtile + (lane & 31)), e);
+        return plan_tile<F, false>(row, lds_addr + (bt % kV3Ring) * kV3Batch + gtile * kSlot, lane, nullptr);
+    };
+    // a logit wave's half of the gathers of one batch, in three stages: half 0
+    // the scale table and pair 0, pairs 1, 2, pair 3; half 1 pairs 4, 5,
+    // pairs 6, 7, pair 8
+    auto issue_stage = [&](const TileGather<false>& g, auto stage) {
+        constexpr int k = decltype(stage)::value;
+        if (ghalf == 0) {
+            if constexpr (k == 0) {
+                issue_scales<F, false>(g, rsrc, lane);
+                issue_blocks<F, 0, 1, false>(g, rsrc);
+            } else if constexpr (k == 1) {
+                issue_blocks<F, 1, 3, false>(g, rsrc);
+            } else {
+                issue_blocks<F, 3, 4, false>(g, rsrc);
+            }
+        } else {
+            if constexpr (k == 0) issue_blocks<F, 4, 6, false>(g, rsrc);
+            else if constexpr (k == 1) issue_blocks<F, 6, 8, false>(g, rsrc);
+            else issue_blocks<F, 8, kRowGathers / 2, false>(g, rsrc);
+        }
+    };
+    // wait until at most this logit wave's gathers of one batch are in flight
+    auto wait_but_one_batch = [&]() {
+        if (ghalf == 0) wait_vmcnt<kScaleInstr + 8>();
+        else wait_vmcnt<10>();
+    };
+    // the prologue part of wave w
+    auto issue_part = [&](int bt, int e) {
+        const TileGather<false> g = plan_batch(bt, e);
+        if (ppart == 0) {
+            issue_scales<F, false>(g, rsrc, lane);
+            issue_blocks<F, 0, 2, false>(g, rsrc);
+        } else if (ppart == 1) {
+            issue_blocks<F, 2, 4, false>(g, rsrc);
+        } else if (ppart == 2) {
+            issue_blocks<F, 4, 6, false>(g, rsrc);
+        } else {
+            issue_blocks<F, 6, kRowGathers / 2, false>(g, rsrc);
+        }
+    };
+
+    // ---- prologue.  Wave 0 copies the entries of batches 0 and 1 into the
+    // free slot 7 and those of batch 2 into its ring rows, then every wave
+    // stages two query rows into the fourth buffer (slot 6).  Once the
+    // entries are visible, all eight waves issue the gathers of batches 0 and 1
+    // (wave w: tile w & 1, part w >> 1 of its gathers), so that no wave waits
+    // for the query before the first rows are requested.
+    const uint32_t pro_entries = lds_addr + 7 * kSlot;
+    if (wave == 0) {
+        if (nb > 0) gather4(4u * (uint32_t)lane, irsrc, pro_entries);
+        if (nb > 1) gather4(4u * (uint32_t)(kV3Tiles * kTile + lane), irsrc, pro_entries + 256);
+        if (nb > 2) stage_entries(2);
+    }
+    {
+        const uint8_t* qblk = (const uint8_t*)(a.q + ((int64_t)b * a.heads + 16 * hb) * kLatent);
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const int h = 2 * wave + r;
+            gather16_global_at<0>(qblk + 1024 * h + 16 * (lane ^ (h & 15)), lds_addr + 3 * kV3Batch + 1024 * h);
+        }
+    }
+    if (wave == 0) wait_vmcnt<2>();   // the entries (the two query rows may still be in flight)
+    if (wave == 4) ((lds_f32*)stats_row(1, lane >> 4))[ln] = -INFINITY;   // bases of "batch -1"
+    lds_barrier();     // the entries of batches 0..2 are visible
+    int e0 = -1, e1 = -1;
+    if (nb > 0) e0 = sanitise(0, ((lds_ci32*)(lds + 7 * kSlot))[lane]);
+    if (nb > 1) e1 = sanitise(1, ((lds_ci32*)(lds + 7 * kSlot + 256))[lane]);
+    if (nb > 0) issue_part(0, e0);
+    if (nb > 1) issue_part(1, e1);
+    if (nb > 1) {
+        // at most this wave's gathers of batch 1 in flight
+        if (ppart == 0) wait_vmcnt<kScaleInstr + 4>();
+        else if (ppart == 3) wait_vmcnt<6>();
+        else wait_vmcnt<4>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    if constexpr (F == SMLA_ROW_UE8M0_SCALES)
+        if (ppart == 0 && nb > 0) expand_ue8m0_scales(lds + gtile * kSlot, lane);
+    lds_barrier();     // batch 0 and the query rows are in LDS
+
+    // The role registers: a logit wave's query operands (16 x 8 bf16: the B
+    // operand of S^T = K . Q^T, lane group q taking columns 16q..16q+15 of
+    // every 64-column group, 8 per K-step, and rope columns 16q..16q+15), a
+    // value wave's output accumulators (the first 8, as 4 fp32 each; the rope
+    // wave's weight sum in the ninth).  One array for both, so that the
+    // register budget holds the larger role, not the sum.
+    u32x4 regs[16];
+    if (wave < 4) {
+        const lds_u8* qs = lds + 3 * kV3Batch;
+#pragma unroll
+        for (int g = 0; g < 7; g++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+                regs[2 * g + ks] = *(lds_cu32x4*)(qs + qstage_addr(ln, 8 * g + 2 * qg + ks));
+        regs[14] = *(lds_cu32x4*)(qs + qstage_addr(ln, 56 + 2 * qg));
+        regs[15] = *(lds_cu32x4*)(qs + qstage_addr(ln, 56 + 2 * qg + 1));
+#pragma unroll
+        for (int k = 0; k < 16; k++) asm volatile("" ::"v"(regs[k]));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; k++) regs[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+    auto qop = [&](int k) { return as_bf16x8(regs[k]); };
+    auto acc_o = [&](int i) { return __builtin_bit_cast(f32x4, regs[i]); };
+    auto set_acc_o = [&](int i, f32x4 v) { regs[i] = __builtin_bit_cast(u32x4, v); };
+
+    // value waves: output columns 128 vi + 16 c + 4 qg .. + 3 of head ln in
+    // block c (nope groups 2vi, 2vi + 1; group 6 and the rope for vi = 3)
+    const int vi = wave - 4;
+    float m_run = -INFINITY;   // running base of head ln (log2 units), the same in every wave
+
+    for (int s = 0; s <= nb; s++) {
+        // the bases of batch s - 1 (-inf for s = 0)
+        float bk[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) bk[j] = ((lds_cf32*)stats_row((s - 1) & 1, j))[ln];
+        const float M = fmaxf(fmaxf(m_run, fmaxf(bk[0], bk[1])), fmaxf(bk[2], bk[3]));
+
+        if (wave < 4) {
+            // ---- logits of half (wave & 1) of tile (wave >> 1) of batch s, with
+            // this wave's gathers of batch s + 2 issued in three stages between
+            // its parts (and before them wave 0's copy of the entries of batch
+            // s + 3)
+            const int qtile = wave >> 1, qhalf = wave & 1;
+            const bool issuing = s + 2 < nb;
+            const int e2 = issuing ? read_entries(s + 2) : -1;
+            TileGather<false> tg = {};
+            if (issuing) {
+                tg = plan_batch(s + 2, e2);
+                if (wave == 0 && s + 3 < nb) stage_entries(s + 3);
+                issue_stage(tg, std::integral_constant<int, 0>{});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < nb) {
+                const lds_u8* st = opaque(lds + (s % kV3Ring) * kV3Batch + qtile * kSlot);
+                lds_cf32* sT = (lds_cf32*)(st + kScaleTable);
+                const int pos = lds_pos(16 * qhalf + ln);
+                const lds_u8* kb = st + piece_addr(qg, pos);
+                u32x4 raw[7], rr[2];
+#pragma unroll
+                for (int g = 0; g < 7; g++) raw[g] = *(lds_cu32x4*)(kb + 2048 * g);
+                rr[0] = *(lds_cu32x4*)(st + piece_addr(kCodePieces + 2 * qg, pos));
+                rr[1] = *(lds_cu32x4*)(st + piece_addr(kCodePieces + 2 * qg + 1, pos));
+                f32x4 acc[8];
+#pragma unroll
+                for (int g = 0; g < 7; g++)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][0], raw[g][1]), qop(2 * g),
+                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[0]), qop(14),
+                                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (issuing) issue_stage(tg, std::integral_constant<int, 1>{});
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < 7; g++)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][2], raw[g][3]),
+                                                                     qop(2 * g + 1), acc[g], 0, 0, 0);
+                acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[1]), qop(15), acc[7], 0, 0, 0);
+                f32x4 v = acc[7];
+#pragma unroll
+                for (int g = 0; g < 7; g++)
+                    v += *(lds_cf32x4*)(sT + g * kTile + lds_pos(16 * qhalf + 4 * qg)) * acc[g];
+                // kept tokens of the tile, by MFMA token
+                const uint64_t vmask =
+                    mask_by_token((__ballot(e0 != -1) >> (32 * qtile)) & 0xFFFFFFFFull) >> (16 * qhalf + 4 * qg);
+                f32x4 z;
+#pragma unroll
+                for (int j = 0; j < 4; j++) z[j] = ((vmask >> j) & 1) ? v[j] * a.logit_factor : -INFINITY;
+                const float mh = lanegroup_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+                // base of this half: the running maximum, or its own maximum when
+                // that is more than kTau above it (weights then stay at most 2^kTau)
+                const float bw = mh > M + kTau ? mh : M;
+                const float be = bw == -INFINITY ? 0.f : bw;
+                f32x4 pw;
+#pragma unroll
+                for (int j = 0; j < 4; j++) pw[j] = __builtin_amdgcn_exp2f(z[j] - be);
+                *(lds_f32x4*)(lds + kV3PTable + (2 * (s & 1) + qtile) * kV3PTile +
+                              ptable_chunk(ln, 4 * qhalf + qg)) = pw;
+                if (qg == 0) ((lds_f32*)stats_row(s & 1, wave))[ln] = bw;
+            } else if (issuing) {
+                issue_stage(tg, std::integral_constant<int, 1>{});
+            }
+            m_run = M;
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- the last stage; then this wave's gathers of batch s + 1 have landed
+            if (issuing) {
+                issue_stage(tg, std::integral_constant<int, 2>{});
+                wait_but_one_batch();
+            } else {
+                wait_vmcnt<0>();
+            }
+            if constexpr (F == SMLA_ROW_UE8M0_SCALES)
+                if (ghalf == 0 && s + 1 < nb)
+                    expand_ue8m0_scales(lds + ((s + 1) % kV3Ring) * kV3Batch + gtile * kSlot, lane);
+            e0 = e1;
+            e1 = e2;
+        } else if (s > 0) {
+            // ---- value product of batch s - 1 over this wave's columns: every
+            // operand of both tiles is read first, then the factors 2^(base - M)
+            // of the four halves are formed, then the products run
+            const lds_u8* const st0 = opaque(lds + ((s - 1) % kV3Ring) * kV3Batch);
+            const lds_u8* const pt0 = lds + kV3PTable + 2 * ((s - 1) & 1) * kV3PTile;
+            auto pvb = [&](auto rope_c) {
+                constexpr bool kRope = decltype(rope_c)::value;   // second group is the rope
+                constexpr int kNope = kRope ? 1 : 2;               // nope groups of this wave
+                const int vpos = lds_pos(8 * qg + (ln >> 1));
+                const int r4 = ln >> 2, c4 = ln & 3;
+                const int rpos0 = lds_pos(8 * qg + r4), rpos1 = lds_pos(8 * qg + 4 + r4);
+                f32x4 P[kV3Tiles][2], S[kV3Tiles][kNope][2];
+                i32x2 V[kV3Tiles][kNope][4];
+                s16x4 R[kV3Tiles][kRope ? 4 : 1][2];
+#pragma unroll
+                for (int tt = 0; tt < kV3Tiles; tt++) {
+                    const lds_u8* st = st0 + tt * kSlot;
+                    const lds_u8* pt = pt0 + tt * kV3PTile;
+                    P[tt][0] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg));
+                    P[tt][1] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg + 1));
+#pragma unroll
+                    for (int gi = 0; gi < kNope; gi++) {
+                        const int g = 2 * vi + gi;
+                        lds_cf32* sT = (lds_cf32*)(st + kScaleTable) + g * kTile;
+                        S[tt][gi][0] = *(lds_cf32x4*)(sT + lds_pos(8 * qg));
+                        S[tt][gi][1] = *(lds_cf32x4*)(sT + lds_pos(8 * qg + 4));
+#pragma unroll
+                        for (int cb = 0; cb < 4; cb++)
+                            V[tt][gi][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                (lds_i32x2*)(st + piece_addr(4 * g + cb, vpos, ln & 1)));
+                    }
+                    if constexpr (kRope) {
+#pragma unroll
+                        for (int dt = 0; dt < 4; dt++) {
+                            const int piece = kCodePieces + 2 * dt + (c4 >> 1);
+                            R[tt][dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_s16x4*)(st + piece_addr(piece, rpos0, c4 & 1)));
+                            R[tt][dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_s16x4*)(st + piece_addr(piece, rpos1, c4 & 1)));
+                        }
+                    }
+                }
+
+                // factors of the halves (0 for a half that kept nothing) and the
+                // rescale of the accumulators when the running maximum rose
+                float fh[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) fh[j] = bk[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(bk[j] - M);
+                const float alpha = M > m_run ? __builtin_amdgcn_exp2f(m_run - M) : 1.f;   // 0 while nothing was kept
+                m_run = M;
+                if (!__all(alpha == 1.f)) {
+#pragma unroll
+                    for (int i = 0; i < (kRope ? 9 : 8); i++) set_acc_o(i, acc_o(i) * alpha);
+                }
+                if (!__all((fh[0] == 1.f) & (fh[1] == 1.f) & (fh[2] == 1.f) & (fh[3] == 1.f))) {
+#pragma unroll
+                    for (int tt = 0; tt < kV3Tiles; tt++) {
+                        const float f = (qg >> 1) ? fh[2 * tt + 1] : fh[2 * tt];
+                        P[tt][0] *= f;
+                        P[tt][1] *= f;
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < kV3Tiles; tt++) {
+                    const f32x4 p0 = P[tt][0], p1 = P[tt][1];
+#pragma unroll
+                    for (int gi = 0; gi < kNope; gi++) {
+                        // weights fp16(p * scale), exact fp8 -> fp16 value codes
+                        const f16x8 bop = weights_f16(p0, p1, S[tt][gi][0], S[tt][gi][1]);
+#pragma unroll
+                        for (int cb = 0; cb < 4; cb++)
+                            set_acc_o(4 * gi + cb, __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                                       codes_to_f16((uint32_t)V[tt][gi][cb][0], (uint32_t)V[tt][gi][cb][1]),
+                                                       bop, acc_o(4 * gi + cb), 0, 0, 0));
+                    }
+                    if constexpr (kRope) {
+                        // rope: bf16 values as stored; weights split into bf16
+                        // high parts and the bf16 of the remainders
+                        u32x4 hi, lo;
+                        hi[0] = pack_bf16x2(p0[0], p0[1]);
+                        hi[1] = pack_bf16x2(p0[2], p0[3]);
+                        hi[2] = pack_bf16x2(p1[0], p1[1]);
+                        hi[3] = pack_bf16x2(p1[2], p1[3]);
+                        lo[0] = pack_bf16x2(p0[0] - __uint_as_float(hi[0] << 16), p0[1] - __uint_as_float(hi[0] & 0xFFFF0000u));
+                        lo[1] = pack_bf16x2(p0[2] - __uint_as_float(hi[1] << 16), p0[3] - __uint_as_float(hi[1] & 0xFFFF0000u));
+                        lo[2] = pack_bf16x2(p1[0] - __uint_as_float(hi[2] << 16), p1[1] - __uint_as_float(hi[2] & 0xFFFF0000u));
+                        lo[3] = pack_bf16x2(p1[2] - __uint_as_float(hi[3] << 16), p1[3] - __uint_as_float(hi[3] & 0xFFFF0000u));
+                        const bf16x8 phi = __builtin_bit_cast(bf16x8, hi), plo = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+                        for (int dt = 0; dt < 4; dt++) {
+                            const bf16x8 aop = __builtin_bit_cast(
+                                bf16x8, __builtin_shufflevector(R[tt][dt][0], R[tt][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                            f32x4 cc = acc_o(4 + dt);
+                            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, cc, 0, 0, 0);
+                            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, cc, 0, 0, 0);
+                            set_acc_o(4 + dt, cc);
+                        }
+                        // the weight sum of head ln as the product with a
+                        // column of ones (every element of block 8 holds it)
+                        const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+                        f32x4 cl = acc_o(8);
+                        cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, phi, cl, 0, 0, 0);
+                        cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, plo, cl, 0, 0, 0);
+                        set_acc_o(8, cl);
+                    }
+                }
+            };
+            if (vi < 3) pvb(std::false_type{});
+            else pvb(std::true_type{});
+        }
+        if (wave >= 4 && s == 0) wait_vmcnt<0>();   // the value waves' gathers of batch 1 (prologue)
+        lds_barrier();   // ends the step
+    }
+
+    // ---- the weight sum of head ln, from the rope wave's product with a
+    // column of ones (through a row that no gather writes)
+    lds_f32* const lsum = (lds_f32*)stats_row(0, 0);
+    if (wave == 7 && qg == 0) lsum[ln] = acc_o(8)[0];
+    lds_barrier();
+    if (wave < 4) return;
+    const float l_run = ((lds_cf32*)lsum)[ln];
+
+    // ---- normalise and write this wave's columns
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const int64_t bh = (int64_t)b * a.heads + head;
+    const bool final_out = a.nsplit == 1 && !a.force_partials;
+    if (final_out) {
+        uint16_t* o = a.out + bh * kLatent + 128 * vi + 4 * qg;
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            u32x2 w;
+            const f32x4 v = acc_o(c) * inv;
+            w[0] = pack_bf16x2(v[0], v[1]);
+            w[1] = pack_bf16x2(v[2], v[3]);
+            *(u32x2*)(o + 16 * c) = w;
+        }
+    } else {
+        float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 128 * vi + 4 * qg;
+#pragma unroll
+        for (int c = 0; c < 8; c++) *(f32x4*)(o + 16 * c) = acc_o(c) * inv;
+    }
+    if (vi == 0 && qg == 0) {
+        const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+        if (final_out) a.lse[bh] = lse;
+        else a.lse_part[bh * a.nsplit + split] = lse;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per-head SIMT decode: the ablation baseline.  The production kernel that the
 // shared-read rewrite replaced ("The Moment of Compilation", section "The
 // Context: A Kernel Optimization Campaign"; "The Power-of-Two Trap", section
@@ -1231,19 +1730,31 @@ int log2_exact(int32_t v) {
 }
 
 constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
+// Longest split list (entries per workgroup) taken by the pipelined kernel on
+// a contiguous cache; longer splits go to the four-wave kernel.  Measured on
+// MI355X (steps of the five benchmark workloads at split counts 1..8): the
+// pipelined kernel is ahead up to 512 entries (its fixed start-up is shorter),
+// the four-wave kernel from 1024 on (its waves stream their own tiles
+// without per-step barriers).
+constexpr int kPipelinedMaxChunk = 512;
 constexpr int kMaxSplits = 4096;     // bound on the split count
 
 // Environment overrides, read once when the library is loaded:
 //   SMLA_NSPLIT=n           split count used when a shape leaves it to the
 //                           library (num_splits == 0), 1 <= n <= kMaxSplits
 //   SMLA_DEBUG_VALIDATE=1   scan the device-resident inputs before every decode
+//   SMLA_KERNEL=four-wave | pipelined
+//                           contiguous-cache kernel for every shape, instead of
+//                           the choice by split length (kPipelinedMaxChunk)
 struct EnvConfig {
     int nsplit;           // 0: the heuristic
     int debug_validate;
+    int kernel;           // 0: by split length, 1: four-wave, 2: pipelined
 };
 
 EnvConfig read_env() {
-    EnvConfig c = {0, 0};
+    EnvConfig c = {0, 0, 0};
+    if (const char* v = getenv("SMLA_KERNEL")) c.kernel = strcmp(v, "four-wave") == 0 ? 1 : strcmp(v, "pipelined") == 0 ? 2 : 0;
     if (const char* v = getenv("SMLA_NSPLIT")) {
         char* end = nullptr;
         const long n = strtol(v, &end, 10);
@@ -1509,14 +2020,26 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     if (g_env.debug_validate && !launch_validate(a, hs)) return SMLA_ERR_HIP;
     if (a.block_table != nullptr) {
         if (!smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs)) return SMLA_ERR_HIP;
-    } else if (a.row_format == SMLA_ROW_UE8M0_SCALES)
-        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args.kv, args.idx, args.seqlens,
-                           args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb, args.heads,
-                           args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
-    else
-        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args.kv, args.idx, args.seqlens,
-                           args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb, args.heads,
-                           args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
+    } else if (g_env.kernel == 1 || (g_env.kernel == 0 && p.chunk > kPipelinedMaxChunk)) {
+        if (a.row_format == SMLA_ROW_UE8M0_SCALES)
+            hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args.kv, args.idx,
+                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
+                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
+        else
+            hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args.kv, args.idx,
+                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
+                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
+    } else {
+        const dim3 blk2(64 * kV3Waves);
+        if (a.row_format == SMLA_ROW_UE8M0_SCALES)
+            hipLaunchKernelGGL((smla_decode_v3_kernel<SMLA_ROW_UE8M0_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
+                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
+                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
+        else
+            hipLaunchKernelGGL((smla_decode_v3_kernel<SMLA_ROW_FP32_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
+                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
+                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
+    }
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
