@@ -285,6 +285,10 @@ def main():
         del src_t, dst_t
         log(f"calibration copy: {args.copy_calibration_mib} MiB read + written")
 
+    # the rotation continues across the warmup and every timed loop, so that
+    # no timed call reuses a copy touched less than R - 1 calls before
+    rot = [0]
+
     def timed(fn, k):
         """k back-to-back calls bracketed by synchronisations; HIP events on the
         launch stream at both ends (no events between launches)."""
@@ -292,16 +296,19 @@ def main():
         b_ev = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
+        i0 = rot[0]
+        rot[0] += k
         a_ev.record(stream)
-        for i in range(k):
+        for i in range(i0, i0 + k):
             fn(i)
         b_ev.record(stream)
         torch.cuda.synchronize()
         return a_ev.elapsed_time(b_ev) / k, (time.perf_counter() - w0) / k * 1e3
 
-    # ---- warmup (untimed)
+    # ---- warmup (untimed), on the first W copies of the rotation
     for i in range(args.warmup):
         step(i)
+    rot[0] = args.warmup
     torch.cuda.synchronize()
 
     # ---- timed region: K whole steps (decode + combine), then K decode launches
@@ -320,9 +327,11 @@ def main():
     kvcold_ms, _ = timed(lambda i: decode_fn(*kvcold_args[i % R]), args.steps)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    i0 = rot[0]
+    rot[0] += args.steps
     evs[0].record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i0 + i)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])

@@ -1054,26 +1054,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
 // ---------------------------------------------------------------------------
 // Pipelined decode kernel (contiguous cache): one workgroup = (sequence b,
 // block hb of 16 heads, split), eight waves in two roles, one of each per
-// SIMD.  The split's list is taken in batches of two 32-token tiles, which
-// move through a ring of four batch buffers in LDS.  In step s:
+// SIMD (waves w and w + 4 share one).  The split's list is taken in batches of
+// two 32-token tiles, which move through a ring of four batch buffers in LDS.
+// In step s:
 //   - the logit waves (0..3) compute S^T for 16-token half (w & 1) of tile
 //     (w >> 1) of batch s against the 16 heads (the bf16 MFMA product of the
 //     four-wave kernel), mask it, take as its base the running maximum, or its
 //     own maximum when that exceeds the running one by more than kTau, and
 //     write its weights p = 2^(z - base) to a weight table and its base per
-//     head to a statistics row;
+//     head to a statistics row; between those parts each issues, in three
+//     stages, its half of the gathers of one tile of batch s + 2 (wave 0 first
+//     copies the list entries of batch s + 3), and at the end waits for its
+//     gathers of batch s + 1;
 //   - the value waves (4..7) accumulate O^T += V^T . P^T for batch s - 1 over
 //     their own output columns (value wave i: nope groups 2i, 2i + 1, or group
 //     6 and the rope for i = 3), each half's weights scaled by 2^(base - M)
-//     (almost always 1: that branch is skipped);
-//   - every wave issues its share of the gathers of batch s + 2 (and wave 0
-//     the copy of the list entries of batch s + 3);
-// and one barrier ends the step, after each wave has waited for its own
-// gathers of batch s + 1.  At the top of every step all eight waves form the
-// same new running maximum M from the four bases of batch s - 1.  The two
-// roles share each SIMD, so one role's memory waits and dependency stalls are
-// filled by the other's work; the weights, not accumulators, cross between
-// waves, and no wave's registers exceed the 256 that two waves per SIMD allow.
+//     (skipped when every factor is 1); they read no memory, only LDS, and the
+//     rope wave also forms the weight sum as the product with a column of ones;
+// and one barrier ends the step.  At its top all eight waves form the same
+// new running maximum M from the four bases of batch s - 1.  The two roles
+// share each SIMD, so one role's waits and dependency stalls are filled by
+// the other's work; the weights, not accumulators, cross between waves, and
+// no wave's registers exceed the 256 that two waves per SIMD allow.
 // Every tile of every batch is gathered (list entries past the split or
 // masked read row -1, i.e. zeros), so no wave ever reads stale bytes and the
 // tile loops carry no branches.
@@ -1084,17 +1086,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
 // bases (slots 4..7).  Every asynchronous memory read of the loop is such a
 // DMA into LDS, so each wave's waits count only its own DMAs.  At the start
 // the fourth buffer stages the workgroup's query (16 rows of 1 KB, read once
-// from memory instead of once per wave).
-constexpr int kV3Waves = 8;
-constexpr int kV3Tiles = 2;                               // tiles per batch
-constexpr int kV3Ring = 4;                                // batch buffers
-constexpr int kV3Batch = kV3Tiles * kSlot;                // 38912 bytes per batch buffer
-constexpr int kV3PTable = kV3Ring * kV3Batch;             // weight tables offset
-constexpr int kV3PTile = 16 * kTile * 4;                  // one tile's weights: [16 heads][32 tokens] fp32
-constexpr int kV3LdsBytes = kV3PTable + 2 * kV3Tiles * kV3PTile;
-static_assert(kV3LdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+// from memory instead of once per wave) and all eight waves gather batches 0
+// and 1.
+constexpr int kPlWaves = 8;
+constexpr int kPlTiles = 2;                               // tiles per batch
+constexpr int kPlRing = 4;                                // batch buffers
+constexpr int kPlBatch = kPlTiles * kSlot;                // 38912 bytes per batch buffer
+constexpr int kPlPTable = kPlRing * kPlBatch;             // weight tables offset
+constexpr int kPlPTile = 16 * kTile * 4;                  // one tile's weights: [16 heads][32 tokens] fp32
+constexpr int kPlLdsBytes = kPlPTable + 2 * kPlTiles * kPlPTile;
+static_assert(kPlLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 static_assert(16 * 1024 <= kScaleTable, "the staged query stays clear of its slot's scale table");
-static_assert(kV3Batch == 2 * kSlot, "slot k of the ring is slot k & 1 of buffer k >> 1");
+static_assert(kPlBatch == 2 * kSlot, "slot k of the ring is slot k & 1 of buffer k >> 1");
 
 // Byte offset in a weight table of tokens 4c..4c+3 of head h in a tile:
 // 16-byte chunks XOR-swizzled by head so that the 16 heads read by one
@@ -1117,16 +1120,8 @@ __device__ __forceinline__ f16x8 weights_f16(f32x4 p0, f32x4 p1, f32x4 s0, f32x4
                  (_Float16)w1[0], (_Float16)w1[1], (_Float16)w1[2], (_Float16)w1[3]};
 }
 
-// Gathers issued per step by the wave of part i (0..3) of a tile: part 0 the
-// scale table and row blocks 0..3, part 1 blocks 4..7, part 2 blocks 8..11,
-// part 3 blocks 12..17 (block pairs j = 2i, 2i + 1, and j = 8 for part 3).
 template <int F>
-__device__ __forceinline__ constexpr int v3_gathers(int part) {
-    return part == 0 ? (F == SMLA_ROW_UE8M0_SCALES ? 1 : kScaleGathers) + 4 : part == 3 ? 6 : 4;
-}
-
-template <int F>
-__global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uint8_t* kv, const int32_t* idx,
+__global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(const uint8_t* kv, const int32_t* idx,
                                                                       const int32_t* seqlens, int64_t kv_seq_stride,
                                                                       int32_t topk, int32_t nsplit, int32_t chunk,
                                                                       int32_t n_hb, int32_t heads,
@@ -1141,7 +1136,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
     a.chunk = chunk;
     a.n_hb = n_hb;
     a.heads = heads;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kV3LdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kPlLdsBytes];
     lds_u8* const lds = (lds_u8*)lds_raw;
     const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
 
@@ -1160,7 +1155,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
     const int head = 16 * hb + ln;
     const int t_begin = split * a.chunk;
     const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
-    const int nb = (n_ent + kV3Tiles * kTile - 1) / (kV3Tiles * kTile);
+    const int nb = (n_ent + kPlTiles * kTile - 1) / (kPlTiles * kTile);
     const int seqlen = (int)min((int64_t)a.seqlens[b], a.kv_seq_stride);
     const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
     const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
@@ -1178,14 +1173,14 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
     // sanitised list entry of batch bt for lane l: tile l >> 5, position l & 31
     // (row -1 past the split, past the sequence or masked)
     auto sanitise = [&](int bt, int v) -> int {
-        return bt * (kV3Tiles * kTile) + lane < n_ent && v >= 0 && v < seqlen ? v : -1;
+        return bt * (kPlTiles * kTile) + lane < n_ent && v >= 0 && v < seqlen ? v : -1;
     };
     // the entries of batch bt in row 7 of slots 2 (bt & 1) and 2 (bt & 1) + 1:
     // copied there by wave 0 (lanes past the split read zeros through the
     // buffer range check), read back by the logit waves
     const i32x4 irsrc = row_rsrc((const uint8_t*)idx_b, 4u * (uint32_t)n_ent);
     auto stage_entries = [&](int bt) {
-        const uint32_t voff = 4u * (uint32_t)(bt * (kV3Tiles * kTile) + lane);
+        const uint32_t voff = 4u * (uint32_t)(bt * (kPlTiles * kTile) + lane);
         const uint32_t row7 = lds_addr + 2 * (bt & 1) * kSlot + kEntryTable;
         if (lane < 32) gather4(voff, irsrc, row7);
         else gather4(voff, irsrc, row7 + kSlot - 4 * 32);
@@ -1199,7 +1194,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
     };
     auto plan_batch = [&](int bt, int e) {
         const int row = __builtin_amdgcn_ds_bpermute(4 * (32 * gtile + (lane & 31)), e);
-        return plan_tile<F, false>(row, lds_addr + (bt % kV3Ring) * kV3Batch + gtile * kSlot, lane, nullptr);
+        return plan_tile<F, false>(row, lds_addr + (bt % kPlRing) * kPlBatch + gtile * kSlot, lane, nullptr);
     };
     // a logit wave's half of the gathers of one batch, in three stages: half 0
     // the scale table and pair 0, pairs 1, 2, pair 3; half 1 pairs 4, 5,
@@ -1250,7 +1245,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
     const uint32_t pro_entries = lds_addr + 7 * kSlot;
     if (wave == 0) {
         if (nb > 0) gather4(4u * (uint32_t)lane, irsrc, pro_entries);
-        if (nb > 1) gather4(4u * (uint32_t)(kV3Tiles * kTile + lane), irsrc, pro_entries + 256);
+        if (nb > 1) gather4(4u * (uint32_t)(kPlTiles * kTile + lane), irsrc, pro_entries + 256);
         if (nb > 2) stage_entries(2);
     }
     {
@@ -1258,7 +1253,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
 #pragma unroll
         for (int r = 0; r < 2; r++) {
             const int h = 2 * wave + r;
-            gather16_global_at<0>(qblk + 1024 * h + 16 * (lane ^ (h & 15)), lds_addr + 3 * kV3Batch + 1024 * h);
+            gather16_global_at<0>(qblk + 1024 * h + 16 * (lane ^ (h & 15)), lds_addr + 3 * kPlBatch + 1024 * h);
         }
     }
     if (wave == 0) wait_vmcnt<2>();   // the entries (the two query rows may still be in flight)
@@ -1289,7 +1284,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
     // register budget holds the larger role, not the sum.
     u32x4 regs[16];
     if (wave < 4) {
-        const lds_u8* qs = lds + 3 * kV3Batch;
+        const lds_u8* qs = lds + 3 * kPlBatch;
 #pragma unroll
         for (int g = 0; g < 7; g++)
 #pragma unroll
@@ -1335,7 +1330,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
             }
             __builtin_amdgcn_sched_barrier(0);
             if (s < nb) {
-                const lds_u8* st = opaque(lds + (s % kV3Ring) * kV3Batch + qtile * kSlot);
+                const lds_u8* st = opaque(lds + (s % kPlRing) * kPlBatch + qtile * kSlot);
                 lds_cf32* sT = (lds_cf32*)(st + kScaleTable);
                 const int pos = lds_pos(16 * qhalf + ln);
                 const lds_u8* kb = st + piece_addr(qg, pos);
@@ -1377,7 +1372,7 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
                 f32x4 pw;
 #pragma unroll
                 for (int j = 0; j < 4; j++) pw[j] = __builtin_amdgcn_exp2f(z[j] - be);
-                *(lds_f32x4*)(lds + kV3PTable + (2 * (s & 1) + qtile) * kV3PTile +
+                *(lds_f32x4*)(lds + kPlPTable + (2 * (s & 1) + qtile) * kPlPTile +
                               ptable_chunk(ln, 4 * qhalf + qg)) = pw;
                 if (qg == 0) ((lds_f32*)stats_row(s & 1, wave))[ln] = bw;
             } else if (issuing) {
@@ -1395,28 +1390,28 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
             }
             if constexpr (F == SMLA_ROW_UE8M0_SCALES)
                 if (ghalf == 0 && s + 1 < nb)
-                    expand_ue8m0_scales(lds + ((s + 1) % kV3Ring) * kV3Batch + gtile * kSlot, lane);
+                    expand_ue8m0_scales(lds + ((s + 1) % kPlRing) * kPlBatch + gtile * kSlot, lane);
             e0 = e1;
             e1 = e2;
         } else if (s > 0) {
             // ---- value product of batch s - 1 over this wave's columns: every
             // operand of both tiles is read first, then the factors 2^(base - M)
             // of the four halves are formed, then the products run
-            const lds_u8* const st0 = opaque(lds + ((s - 1) % kV3Ring) * kV3Batch);
-            const lds_u8* const pt0 = lds + kV3PTable + 2 * ((s - 1) & 1) * kV3PTile;
+            const lds_u8* const st0 = opaque(lds + ((s - 1) % kPlRing) * kPlBatch);
+            const lds_u8* const pt0 = lds + kPlPTable + 2 * ((s - 1) & 1) * kPlPTile;
             auto pvb = [&](auto rope_c) {
                 constexpr bool kRope = decltype(rope_c)::value;   // second group is the rope
                 constexpr int kNope = kRope ? 1 : 2;               // nope groups of this wave
                 const int vpos = lds_pos(8 * qg + (ln >> 1));
                 const int r4 = ln >> 2, c4 = ln & 3;
                 const int rpos0 = lds_pos(8 * qg + r4), rpos1 = lds_pos(8 * qg + 4 + r4);
-                f32x4 P[kV3Tiles][2], S[kV3Tiles][kNope][2];
-                i32x2 V[kV3Tiles][kNope][4];
-                s16x4 R[kV3Tiles][kRope ? 4 : 1][2];
+                f32x4 P[kPlTiles][2], S[kPlTiles][kNope][2];
+                i32x2 V[kPlTiles][kNope][4];
+                s16x4 R[kPlTiles][kRope ? 4 : 1][2];
 #pragma unroll
-                for (int tt = 0; tt < kV3Tiles; tt++) {
+                for (int tt = 0; tt < kPlTiles; tt++) {
                     const lds_u8* st = st0 + tt * kSlot;
-                    const lds_u8* pt = pt0 + tt * kV3PTile;
+                    const lds_u8* pt = pt0 + tt * kPlPTile;
                     P[tt][0] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg));
                     P[tt][1] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg + 1));
 #pragma unroll
@@ -1455,14 +1450,14 @@ __global__ __launch_bounds__(64 * kV3Waves) void smla_decode_v3_kernel(const uin
                 }
                 if (!__all((fh[0] == 1.f) & (fh[1] == 1.f) & (fh[2] == 1.f) & (fh[3] == 1.f))) {
 #pragma unroll
-                    for (int tt = 0; tt < kV3Tiles; tt++) {
+                    for (int tt = 0; tt < kPlTiles; tt++) {
                         const float f = (qg >> 1) ? fh[2 * tt + 1] : fh[2 * tt];
                         P[tt][0] *= f;
                         P[tt][1] *= f;
                     }
                 }
 #pragma unroll
-                for (int tt = 0; tt < kV3Tiles; tt++) {
+                for (int tt = 0; tt < kPlTiles; tt++) {
                     const f32x4 p0 = P[tt][0], p1 = P[tt][1];
 #pragma unroll
                     for (int gi = 0; gi < kNope; gi++) {
@@ -2030,13 +2025,13 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
                                args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
                                args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
     } else {
-        const dim3 blk2(64 * kV3Waves);
+        const dim3 blk2(64 * kPlWaves);
         if (a.row_format == SMLA_ROW_UE8M0_SCALES)
-            hipLaunchKernelGGL((smla_decode_v3_kernel<SMLA_ROW_UE8M0_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
+            hipLaunchKernelGGL((smla_decode_pipelined_kernel<SMLA_ROW_UE8M0_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
                                args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
                                args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
         else
-            hipLaunchKernelGGL((smla_decode_v3_kernel<SMLA_ROW_FP32_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
+            hipLaunchKernelGGL((smla_decode_pipelined_kernel<SMLA_ROW_FP32_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
                                args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
                                args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
     }
