@@ -1276,45 +1276,35 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
         if (ppart == 0 && nb > 0) expand_ue8m0_scales(lds + gtile * kSlot, lane);
     lds_barrier();     // batch 0 and the query rows are in LDS
 
-    // The role registers: a logit wave's query operands (16 x 8 bf16: the B
-    // operand of S^T = K . Q^T, lane group q taking columns 16q..16q+15 of
-    // every 64-column group, 8 per K-step, and rope columns 16q..16q+15), a
-    // value wave's output accumulators (the first 8, as 4 fp32 each; the rope
-    // wave's weight sum in the ninth).  One array for both, so that the
-    // register budget holds the larger role, not the sum.
-    u32x4 regs[16];
+    // Each role runs its own loop over the steps (the same barriers: one per
+    // step, then one for the weight sum), and each kind of value wave its own
+    // copy of the value loop, so that a wave's registers keep their values
+    // across the steps instead of being merged (copied) between code paths.
+    const int vi = wave - 4;   // value waves: output columns 128 vi + 16 c + 4 qg .. + 3 of head ln in
+                               // block c (nope groups 2vi, 2vi + 1; group 6 and the rope for vi = 3)
+    lds_f32* const lsum = (lds_f32*)stats_row(0, 0);   // the weight sum (after the loop)
     if (wave < 4) {
-        const lds_u8* qs = lds + 3 * kPlBatch;
+        // ---- logit wave: the query operands (16 x 8 bf16: the B operand of
+        // S^T = K . Q^T, lane group q taking columns 16q..16q+15 of every
+        // 64-column group, 8 per K-step, and rope columns 16q..16q+15)
+        bf16x8 qop[16];
+        {
+            const lds_u8* qs = lds + 3 * kPlBatch;
 #pragma unroll
-        for (int g = 0; g < 7; g++)
+            for (int g = 0; g < 7; g++)
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++)
-                regs[2 * g + ks] = *(lds_cu32x4*)(qs + qstage_addr(ln, 8 * g + 2 * qg + ks));
-        regs[14] = *(lds_cu32x4*)(qs + qstage_addr(ln, 56 + 2 * qg));
-        regs[15] = *(lds_cu32x4*)(qs + qstage_addr(ln, 56 + 2 * qg + 1));
+                for (int ks = 0; ks < 2; ks++)
+                    qop[2 * g + ks] = as_bf16x8(*(lds_cu32x4*)(qs + qstage_addr(ln, 8 * g + 2 * qg + ks)));
+            qop[14] = as_bf16x8(*(lds_cu32x4*)(qs + qstage_addr(ln, 56 + 2 * qg)));
+            qop[15] = as_bf16x8(*(lds_cu32x4*)(qs + qstage_addr(ln, 56 + 2 * qg + 1)));
+        }
+        float m_run = -INFINITY;   // running base of head ln (log2 units), the same in every wave
+        for (int s = 0; s <= nb; s++) {
+            // the bases of batch s - 1 (-inf for s = 0)
+            float bk[4];
 #pragma unroll
-        for (int k = 0; k < 16; k++) asm volatile("" ::"v"(regs[k]));
-    } else {
-#pragma unroll
-        for (int k = 0; k < 16; k++) regs[k] = u32x4{0u, 0u, 0u, 0u};
-    }
-    auto qop = [&](int k) { return as_bf16x8(regs[k]); };
-    auto acc_o = [&](int i) { return __builtin_bit_cast(f32x4, regs[i]); };
-    auto set_acc_o = [&](int i, f32x4 v) { regs[i] = __builtin_bit_cast(u32x4, v); };
-
-    // value waves: output columns 128 vi + 16 c + 4 qg .. + 3 of head ln in
-    // block c (nope groups 2vi, 2vi + 1; group 6 and the rope for vi = 3)
-    const int vi = wave - 4;
-    float m_run = -INFINITY;   // running base of head ln (log2 units), the same in every wave
-
-    for (int s = 0; s <= nb; s++) {
-        // the bases of batch s - 1 (-inf for s = 0)
-        float bk[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) bk[j] = ((lds_cf32*)stats_row((s - 1) & 1, j))[ln];
-        const float M = fmaxf(fmaxf(m_run, fmaxf(bk[0], bk[1])), fmaxf(bk[2], bk[3]));
-
-        if (wave < 4) {
+            for (int j = 0; j < 4; j++) bk[j] = ((lds_cf32*)stats_row((s - 1) & 1, j))[ln];
+            const float M = fmaxf(fmaxf(m_run, fmaxf(bk[0], bk[1])), fmaxf(bk[2], bk[3]));
             // ---- logits of half (wave & 1) of tile (wave >> 1) of batch s, with
             // this wave's gathers of batch s + 2 issued in three stages between
             // its parts (and before them wave 0's copy of the entries of batch
@@ -1342,9 +1332,9 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
                 f32x4 acc[8];
 #pragma unroll
                 for (int g = 0; g < 7; g++)
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][0], raw[g][1]), qop(2 * g),
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][0], raw[g][1]), qop[2 * g],
                                                                      f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[0]), qop(14),
+                acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[0]), qop[14],
                                                                  f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 if (issuing) issue_stage(tg, std::integral_constant<int, 1>{});
@@ -1352,8 +1342,8 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
 #pragma unroll
                 for (int g = 0; g < 7; g++)
                     acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(raw[g][2], raw[g][3]),
-                                                                     qop(2 * g + 1), acc[g], 0, 0, 0);
-                acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[1]), qop(15), acc[7], 0, 0, 0);
+                                                                     qop[2 * g + 1], acc[g], 0, 0, 0);
+                acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rr[1]), qop[15], acc[7], 0, 0, 0);
                 f32x4 v = acc[7];
 #pragma unroll
                 for (int g = 0; g < 7; g++)
@@ -1393,153 +1383,166 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
                     expand_ue8m0_scales(lds + ((s + 1) % kPlRing) * kPlBatch + gtile * kSlot, lane);
             e0 = e1;
             e1 = e2;
-        } else if (s > 0) {
+            lds_barrier();   // ends the step
+        }
+        lds_barrier();   // the weight sum is written
+        return;
+    }
+
+    auto value_loop = [&](auto rope_c) {
+        constexpr bool kRope = decltype(rope_c)::value;   // second group is the rope
+        constexpr int kNope = kRope ? 1 : 2;               // nope groups of this wave
+        // the accumulators (and the rope wave's weight sum in the ninth)
+        f32x4 acc[kRope ? 9 : 8];
+#pragma unroll
+        for (int i = 0; i < (kRope ? 9 : 8); i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY;
+        wait_vmcnt<0>();   // step 0: this wave's gathers of batch 1 (prologue)
+        lds_barrier();
+        for (int s = 1; s <= nb; s++) {
+            // the bases of batch s - 1
+            float bk[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) bk[j] = ((lds_cf32*)stats_row((s - 1) & 1, j))[ln];
+            const float M = fmaxf(fmaxf(m_run, fmaxf(bk[0], bk[1])), fmaxf(bk[2], bk[3]));
             // ---- value product of batch s - 1 over this wave's columns: every
             // operand of both tiles is read first, then the factors 2^(base - M)
             // of the four halves are formed, then the products run
             const lds_u8* const st0 = opaque(lds + ((s - 1) % kPlRing) * kPlBatch);
             const lds_u8* const pt0 = lds + kPlPTable + 2 * ((s - 1) & 1) * kPlPTile;
-            auto pvb = [&](auto rope_c) {
-                constexpr bool kRope = decltype(rope_c)::value;   // second group is the rope
-                constexpr int kNope = kRope ? 1 : 2;               // nope groups of this wave
-                const int vpos = lds_pos(8 * qg + (ln >> 1));
-                const int r4 = ln >> 2, c4 = ln & 3;
-                const int rpos0 = lds_pos(8 * qg + r4), rpos1 = lds_pos(8 * qg + 4 + r4);
-                f32x4 P[kPlTiles][2], S[kPlTiles][kNope][2];
-                i32x2 V[kPlTiles][kNope][4];
-                s16x4 R[kPlTiles][kRope ? 4 : 1][2];
+            const int vpos = lds_pos(8 * qg + (ln >> 1));
+            const int r4 = ln >> 2, c4 = ln & 3;
+            const int rpos0 = lds_pos(8 * qg + r4), rpos1 = lds_pos(8 * qg + 4 + r4);
+            f32x4 P[kPlTiles][2], S[kPlTiles][kNope][2];
+            i32x2 V[kPlTiles][kNope][4];
+            s16x4 R[kPlTiles][kRope ? 4 : 1][2];
 #pragma unroll
-                for (int tt = 0; tt < kPlTiles; tt++) {
-                    const lds_u8* st = st0 + tt * kSlot;
-                    const lds_u8* pt = pt0 + tt * kPlPTile;
-                    P[tt][0] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg));
-                    P[tt][1] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg + 1));
+            for (int tt = 0; tt < kPlTiles; tt++) {
+                const lds_u8* st = st0 + tt * kSlot;
+                const lds_u8* pt = pt0 + tt * kPlPTile;
+                P[tt][0] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg));
+                P[tt][1] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg + 1));
 #pragma unroll
-                    for (int gi = 0; gi < kNope; gi++) {
-                        const int g = 2 * vi + gi;
-                        lds_cf32* sT = (lds_cf32*)(st + kScaleTable) + g * kTile;
-                        S[tt][gi][0] = *(lds_cf32x4*)(sT + lds_pos(8 * qg));
-                        S[tt][gi][1] = *(lds_cf32x4*)(sT + lds_pos(8 * qg + 4));
+                for (int gi = 0; gi < kNope; gi++) {
+                    const int g = 2 * vi + gi;
+                    lds_cf32* sT = (lds_cf32*)(st + kScaleTable) + g * kTile;
+                    S[tt][gi][0] = *(lds_cf32x4*)(sT + lds_pos(8 * qg));
+                    S[tt][gi][1] = *(lds_cf32x4*)(sT + lds_pos(8 * qg + 4));
 #pragma unroll
-                        for (int cb = 0; cb < 4; cb++)
-                            V[tt][gi][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                                (lds_i32x2*)(st + piece_addr(4 * g + cb, vpos, ln & 1)));
-                    }
-                    if constexpr (kRope) {
+                    for (int cb = 0; cb < 4; cb++)
+                        V[tt][gi][cb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (lds_i32x2*)(st + piece_addr(4 * g + cb, vpos, ln & 1)));
+                }
+                if constexpr (kRope) {
 #pragma unroll
-                        for (int dt = 0; dt < 4; dt++) {
-                            const int piece = kCodePieces + 2 * dt + (c4 >> 1);
-                            R[tt][dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_s16x4*)(st + piece_addr(piece, rpos0, c4 & 1)));
-                            R[tt][dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_s16x4*)(st + piece_addr(piece, rpos1, c4 & 1)));
-                        }
+                    for (int dt = 0; dt < 4; dt++) {
+                        const int piece = kCodePieces + 2 * dt + (c4 >> 1);
+                        R[tt][dt][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(st + piece_addr(piece, rpos0, c4 & 1)));
+                        R[tt][dt][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)(st + piece_addr(piece, rpos1, c4 & 1)));
                     }
                 }
+            }
 
-                // factors of the halves (0 for a half that kept nothing) and the
-                // rescale of the accumulators when the running maximum rose
-                float fh[4];
+            // factors of the halves (0 for a half that kept nothing) and the
+            // rescale of the accumulators when the running maximum rose
+            float fh[4];
 #pragma unroll
-                for (int j = 0; j < 4; j++) fh[j] = bk[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(bk[j] - M);
-                const float alpha = M > m_run ? __builtin_amdgcn_exp2f(m_run - M) : 1.f;   // 0 while nothing was kept
-                m_run = M;
-                if (!__all(alpha == 1.f)) {
+            for (int j = 0; j < 4; j++) fh[j] = bk[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(bk[j] - M);
+            const float alpha = M > m_run ? __builtin_amdgcn_exp2f(m_run - M) : 1.f;   // 0 while nothing was kept
+            m_run = M;
+            if (!__all(alpha == 1.f)) {
 #pragma unroll
-                    for (int i = 0; i < (kRope ? 9 : 8); i++) set_acc_o(i, acc_o(i) * alpha);
+                for (int i = 0; i < (kRope ? 9 : 8); i++) acc[i] *= alpha;
+            }
+            // (unconditional: a branch here would split the value
+            // product's instruction stream, and p * 1 is exact)
+#pragma unroll
+            for (int tt = 0; tt < kPlTiles; tt++) {
+                const float f = (qg >> 1) ? fh[2 * tt + 1] : fh[2 * tt];
+                P[tt][0] *= f;
+                P[tt][1] *= f;
+            }
+#pragma unroll
+            for (int tt = 0; tt < kPlTiles; tt++) {
+                const f32x4 p0 = P[tt][0], p1 = P[tt][1];
+#pragma unroll
+                for (int gi = 0; gi < kNope; gi++) {
+                    // weights fp16(p * scale), exact fp8 -> fp16 value codes
+                    const f16x8 bop = weights_f16(p0, p1, S[tt][gi][0], S[tt][gi][1]);
+#pragma unroll
+                    for (int cb = 0; cb < 4; cb++)
+                        acc[4 * gi + cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            codes_to_f16((uint32_t)V[tt][gi][cb][0], (uint32_t)V[tt][gi][cb][1]), bop,
+                            acc[4 * gi + cb], 0, 0, 0);
                 }
-                if (!__all((fh[0] == 1.f) & (fh[1] == 1.f) & (fh[2] == 1.f) & (fh[3] == 1.f))) {
+                if constexpr (kRope) {
+                    // rope: bf16 values as stored; weights split into bf16
+                    // high parts and the bf16 of the remainders
+                    u32x4 hi, lo;
+                    hi[0] = pack_bf16x2(p0[0], p0[1]);
+                    hi[1] = pack_bf16x2(p0[2], p0[3]);
+                    hi[2] = pack_bf16x2(p1[0], p1[1]);
+                    hi[3] = pack_bf16x2(p1[2], p1[3]);
+                    lo[0] = pack_bf16x2(p0[0] - __uint_as_float(hi[0] << 16), p0[1] - __uint_as_float(hi[0] & 0xFFFF0000u));
+                    lo[1] = pack_bf16x2(p0[2] - __uint_as_float(hi[1] << 16), p0[3] - __uint_as_float(hi[1] & 0xFFFF0000u));
+                    lo[2] = pack_bf16x2(p1[0] - __uint_as_float(hi[2] << 16), p1[1] - __uint_as_float(hi[2] & 0xFFFF0000u));
+                    lo[3] = pack_bf16x2(p1[2] - __uint_as_float(hi[3] << 16), p1[3] - __uint_as_float(hi[3] & 0xFFFF0000u));
+                    const bf16x8 phi = __builtin_bit_cast(bf16x8, hi), plo = __builtin_bit_cast(bf16x8, lo);
 #pragma unroll
-                    for (int tt = 0; tt < kPlTiles; tt++) {
-                        const float f = (qg >> 1) ? fh[2 * tt + 1] : fh[2 * tt];
-                        P[tt][0] *= f;
-                        P[tt][1] *= f;
+                    for (int dt = 0; dt < 4; dt++) {
+                        const bf16x8 aop = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(R[tt][dt][0], R[tt][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                        f32x4 cc = acc[4 + dt];
+                        cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, cc, 0, 0, 0);
+                        cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, cc, 0, 0, 0);
+                        acc[4 + dt] = cc;
                     }
+                    // the weight sum of head ln as the product with a
+                    // column of ones (every element of block 8 holds it)
+                    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+                    f32x4 cl = acc[8];
+                    cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, phi, cl, 0, 0, 0);
+                    cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, plo, cl, 0, 0, 0);
+                    acc[8] = cl;
                 }
-#pragma unroll
-                for (int tt = 0; tt < kPlTiles; tt++) {
-                    const f32x4 p0 = P[tt][0], p1 = P[tt][1];
-#pragma unroll
-                    for (int gi = 0; gi < kNope; gi++) {
-                        // weights fp16(p * scale), exact fp8 -> fp16 value codes
-                        const f16x8 bop = weights_f16(p0, p1, S[tt][gi][0], S[tt][gi][1]);
-#pragma unroll
-                        for (int cb = 0; cb < 4; cb++)
-                            set_acc_o(4 * gi + cb, __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                                       codes_to_f16((uint32_t)V[tt][gi][cb][0], (uint32_t)V[tt][gi][cb][1]),
-                                                       bop, acc_o(4 * gi + cb), 0, 0, 0));
-                    }
-                    if constexpr (kRope) {
-                        // rope: bf16 values as stored; weights split into bf16
-                        // high parts and the bf16 of the remainders
-                        u32x4 hi, lo;
-                        hi[0] = pack_bf16x2(p0[0], p0[1]);
-                        hi[1] = pack_bf16x2(p0[2], p0[3]);
-                        hi[2] = pack_bf16x2(p1[0], p1[1]);
-                        hi[3] = pack_bf16x2(p1[2], p1[3]);
-                        lo[0] = pack_bf16x2(p0[0] - __uint_as_float(hi[0] << 16), p0[1] - __uint_as_float(hi[0] & 0xFFFF0000u));
-                        lo[1] = pack_bf16x2(p0[2] - __uint_as_float(hi[1] << 16), p0[3] - __uint_as_float(hi[1] & 0xFFFF0000u));
-                        lo[2] = pack_bf16x2(p1[0] - __uint_as_float(hi[2] << 16), p1[1] - __uint_as_float(hi[2] & 0xFFFF0000u));
-                        lo[3] = pack_bf16x2(p1[2] - __uint_as_float(hi[3] << 16), p1[3] - __uint_as_float(hi[3] & 0xFFFF0000u));
-                        const bf16x8 phi = __builtin_bit_cast(bf16x8, hi), plo = __builtin_bit_cast(bf16x8, lo);
-#pragma unroll
-                        for (int dt = 0; dt < 4; dt++) {
-                            const bf16x8 aop = __builtin_bit_cast(
-                                bf16x8, __builtin_shufflevector(R[tt][dt][0], R[tt][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                            f32x4 cc = acc_o(4 + dt);
-                            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, cc, 0, 0, 0);
-                            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, cc, 0, 0, 0);
-                            set_acc_o(4 + dt, cc);
-                        }
-                        // the weight sum of head ln as the product with a
-                        // column of ones (every element of block 8 holds it)
-                        const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-                        f32x4 cl = acc_o(8);
-                        cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, phi, cl, 0, 0, 0);
-                        cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, plo, cl, 0, 0, 0);
-                        set_acc_o(8, cl);
-                    }
-                }
-            };
-            if (vi < 3) pvb(std::false_type{});
-            else pvb(std::true_type{});
+            }
+            lds_barrier();   // ends the step
         }
-        if (wave >= 4 && s == 0) wait_vmcnt<0>();   // the value waves' gathers of batch 1 (prologue)
-        lds_barrier();   // ends the step
-    }
-
-    // ---- the weight sum of head ln, from the rope wave's product with a
-    // column of ones (through a row that no gather writes)
-    lds_f32* const lsum = (lds_f32*)stats_row(0, 0);
-    if (wave == 7 && qg == 0) lsum[ln] = acc_o(8)[0];
-    lds_barrier();
-    if (wave < 4) return;
-    const float l_run = ((lds_cf32*)lsum)[ln];
-
-    // ---- normalise and write this wave's columns
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t bh = (int64_t)b * a.heads + head;
-    const bool final_out = a.nsplit == 1 && !a.force_partials;
-    if (final_out) {
-        uint16_t* o = a.out + bh * kLatent + 128 * vi + 4 * qg;
+        // ---- the weight sum of head ln, from the rope wave's product with a
+        // column of ones (through a row that no gather writes)
+        if constexpr (kRope)
+            if (qg == 0) lsum[ln] = acc[8][0];
+        lds_barrier();
+        const float l_run = ((lds_cf32*)lsum)[ln];
+        // ---- normalise and write this wave's columns
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        const int64_t bh = (int64_t)b * a.heads + head;
+        const bool final_out = a.nsplit == 1 && !a.force_partials;
+        if (final_out) {
+            uint16_t* o = a.out + bh * kLatent + 128 * vi + 4 * qg;
 #pragma unroll
-        for (int c = 0; c < 8; c++) {
-            u32x2 w;
-            const f32x4 v = acc_o(c) * inv;
-            w[0] = pack_bf16x2(v[0], v[1]);
-            w[1] = pack_bf16x2(v[2], v[3]);
-            *(u32x2*)(o + 16 * c) = w;
+            for (int c = 0; c < 8; c++) {
+                u32x2 w;
+                const f32x4 v = acc[c] * inv;
+                w[0] = pack_bf16x2(v[0], v[1]);
+                w[1] = pack_bf16x2(v[2], v[3]);
+                *(u32x2*)(o + 16 * c) = w;
+            }
+        } else {
+            float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 128 * vi + 4 * qg;
+#pragma unroll
+            for (int c = 0; c < 8; c++) *(f32x4*)(o + 16 * c) = acc[c] * inv;
         }
-    } else {
-        float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 128 * vi + 4 * qg;
-#pragma unroll
-        for (int c = 0; c < 8; c++) *(f32x4*)(o + 16 * c) = acc_o(c) * inv;
-    }
-    if (vi == 0 && qg == 0) {
-        const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-        if (final_out) a.lse[bh] = lse;
-        else a.lse_part[bh * a.nsplit + split] = lse;
-    }
+        if (vi == 0 && qg == 0) {
+            const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+            if (final_out) a.lse[bh] = lse;
+            else a.lse_part[bh * a.nsplit + split] = lse;
+        }
+    };
+    if (vi < 3) value_loop(std::false_type{});
+    else value_loop(std::true_type{});
 }
 
 // ---------------------------------------------------------------------------
