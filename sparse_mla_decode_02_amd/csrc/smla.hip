@@ -1089,6 +1089,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
 // from memory instead of once per wave) and all eight waves gather batches 0
 // and 1.
 constexpr int kPlWaves = 8;
+constexpr int kPlPagedBatches = 8;                        // batches of a split on a paged pool (512 entries)
+constexpr int kPlBtLds = 8192;                            // block-table slots copied into LDS (32 KB)
 constexpr int kPlTiles = 2;                               // tiles per batch
 constexpr int kPlRing = 4;                                // batch buffers
 constexpr int kPlBatch = kPlTiles * kSlot;                // 38912 bytes per batch buffer
@@ -1098,6 +1100,7 @@ constexpr int kPlLdsBytes = kPlPTable + 2 * kPlTiles * kPlPTile;
 static_assert(kPlLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 static_assert(16 * 1024 <= kScaleTable, "the staged query stays clear of its slot's scale table");
 static_assert(kPlBatch == 2 * kSlot, "slot k of the ring is slot k & 1 of buffer k >> 1");
+static_assert(4 * kPlBtLds <= kPlBatch, "a paged prologue's block-table row fits the third batch buffer");
 
 // Byte offset in a weight table of tokens 4c..4c+3 of head h in a tile:
 // 16-byte chunks XOR-swizzled by head so that the 16 heads read by one
@@ -1120,7 +1123,7 @@ __device__ __forceinline__ f16x8 weights_f16(f32x4 p0, f32x4 p1, f32x4 s0, f32x4
                  (_Float16)w1[0], (_Float16)w1[1], (_Float16)w1[2], (_Float16)w1[3]};
 }
 
-template <int F>
+template <int F, bool P>
 __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(const uint8_t* kv, const int32_t* idx,
                                                                       const int32_t* seqlens, int64_t kv_seq_stride,
                                                                       int32_t topk, int32_t nsplit, int32_t chunk,
@@ -1156,8 +1159,12 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
     const int t_begin = split * a.chunk;
     const int n_ent = max(min(a.topk, t_begin + a.chunk) - t_begin, 0);
     const int nb = (n_ent + kPlTiles * kTile - 1) / (kPlTiles * kTile);
-    const int seqlen = (int)min((int64_t)a.seqlens[b], a.kv_seq_stride);
-    const i32x4 rsrc = row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
+    const int seqlen = P ? a.seqlens[b] : (int)min((int64_t)a.seqlens[b], a.kv_seq_stride);
+    // rows through one buffer resource: the sequence's rows, or (paged) the
+    // whole pool, below 2^31 bytes (pool rows then fit the 24-bit multiply of
+    // row_offset)
+    const i32x4 rsrc = P ? row_rsrc(a.kv, a.pool_rows * (uint32_t)RowFormat<F>::kBytes)
+                         : row_rsrc(a.kv + (int64_t)b * a.kv_seq_stride * RowFormat<F>::kBytes, a.seq_bytes);
     const int32_t* idx_b = a.idx + (int64_t)b * a.topk + t_begin;
 
     // In the loop, logit wave w issues the gathers of tile w & 1 of each batch:
@@ -1243,25 +1250,93 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
     // (wave w: tile w & 1, part w >> 1 of its gathers), so that no wave waits
     // for the query before the first rows are requested.
     const uint32_t pro_entries = lds_addr + 7 * kSlot;
-    if (wave == 0) {
+    if (!P && wave == 0) {
         if (nb > 0) gather4(4u * (uint32_t)lane, irsrc, pro_entries);
         if (nb > 1) gather4(4u * (uint32_t)(kPlTiles * kTile + lane), irsrc, pro_entries + 256);
         if (nb > 2) stage_entries(2);
     }
-    {
+    auto stage_query = [&]() {
         const uint8_t* qblk = (const uint8_t*)(a.q + ((int64_t)b * a.heads + 16 * hb) * kLatent);
 #pragma unroll
         for (int r = 0; r < 2; r++) {
             const int h = 2 * wave + r;
             gather16_global_at<0>(qblk + 1024 * h + 16 * (lane ^ (h & 15)), lds_addr + 3 * kPlBatch + 1024 * h);
         }
+    };
+    if (!P) stage_query();
+    // Paged pool: a kept entry e of the sequence is at pool row
+    // (block_table[b][e >> page_shift] << page_shift) + (e & (page - 1)).  A
+    // split of this kernel holds at most kPlPagedBatches batches, so every
+    // lane translates its entry of each batch here, once, and keeps the pool
+    // rows in registers: lane l, batch k: tile l >> 5, position l & 31; -1 for
+    // a masked entry, a page past the table row or a slot outside the pool.
+    // The sequence's block-table row does not depend on the entries: up to
+    // kPlBtLds pages it is copied into the third batch buffer (free until step
+    // 0) while the entries load, so the translation costs no second memory
+    // round trip; a longer row is read entry by entry after the entries.
+    int prow[P ? kPlPagedBatches : 1];
+    int pe[P ? kPlPagedBatches : 1];
+    const int32_t* const bt_b = P ? a.block_table + (int64_t)b * a.pages_per_seq : nullptr;
+    const bool bt_in_lds = P && a.pages_per_seq <= kPlBtLds;
+    if constexpr (P) {
+        if (bt_in_lds) {
+            const i32x4 btrsrc = row_rsrc((const uint8_t*)bt_b, 4u * (uint32_t)a.pages_per_seq);
+            const int n_copy = (a.pages_per_seq + 63) / 64;   // 64 slots per copy; lanes past the row read zeros
+            for (int k = wave; k < n_copy; k += kPlWaves)
+                gather4(4u * (uint32_t)(64 * k + lane), btrsrc, lds_addr + 2 * kPlBatch + 256 * k);
+        }
+        // every batch's entry loaded at once (clamped into the split's list:
+        // loads in per-batch branches would each wait for the one before)
+        int raw[kPlPagedBatches];
+        if (nb > 0) {
+#pragma unroll
+            for (int k = 0; k < kPlPagedBatches; k++) raw[k] = idx_b[min(k * kPlTiles * kTile + lane, n_ent - 1)];
+        }
+#pragma unroll
+        for (int k = 0; k < kPlPagedBatches; k++) pe[k] = k < nb ? sanitise(k, raw[k]) : -1;
+        wait_vmcnt<0>();   // the entries and this wave's share of the block-table row
+#pragma unroll
+        for (int k = 0; k < kPlPagedBatches; k++) asm volatile("" ::"v"(pe[k]));
+        // the query rows only now, so that no wait above includes them: they
+        // land while the first batches are gathered
+        stage_query();
     }
-    if (wave == 0) wait_vmcnt<2>();   // the entries (the two query rows may still be in flight)
+    // the pool rows of batch bt (a uniform index)
+    auto prow_of = [&](int bt) -> int {
+        int r = prow[0];
+#pragma unroll
+        for (int k = 1; k < (P ? kPlPagedBatches : 1); k++) r = bt == k ? prow[k] : r;
+        return r;
+    };
+    if (!P && wave == 0) wait_vmcnt<2>();   // the entries (the two query rows may still be in flight)
     if (wave == 4) ((lds_f32*)stats_row(1, lane >> 4))[ln] = -INFINITY;   // bases of "batch -1"
-    lds_barrier();     // the entries of batches 0..2 are visible
+    lds_barrier();     // the entries of batches 0..2 (paged: the block-table row) are visible
     int e0 = -1, e1 = -1;
-    if (nb > 0) e0 = sanitise(0, ((lds_ci32*)(lds + 7 * kSlot))[lane]);
-    if (nb > 1) e1 = sanitise(1, ((lds_ci32*)(lds + 7 * kSlot + 256))[lane]);
+    if constexpr (P) {
+        int pg[kPlPagedBatches], slot[kPlPagedBatches];
+#pragma unroll
+        for (int k = 0; k < kPlPagedBatches; k++) slot[k] = pe[k] >= 0 ? min(pe[k] >> a.page_shift, a.pages_per_seq - 1) : 0;
+        if (bt_in_lds) {
+            const lds_ci32* const bt_lds = (lds_ci32*)(lds + 2 * kPlBatch);
+#pragma unroll
+            for (int k = 0; k < kPlPagedBatches; k++) pg[k] = bt_lds[slot[k]];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPlPagedBatches; k++) pg[k] = bt_b[slot[k]];   // all at once, as the entries
+        }
+        const uint32_t page_mask = (1u << a.page_shift) - 1u;
+#pragma unroll
+        for (int k = 0; k < kPlPagedBatches; k++)
+            prow[k] = k < nb && pe[k] >= 0 && (pe[k] >> a.page_shift) < a.pages_per_seq && pg[k] >= 0 &&
+                              (uint32_t)pg[k] < (a.pool_rows >> a.page_shift)
+                          ? (int)(((uint32_t)pg[k] << a.page_shift) | ((uint32_t)pe[k] & page_mask))
+                          : -1;
+        e0 = prow[0];
+        e1 = prow_of(1);
+    } else {
+        if (nb > 0) e0 = sanitise(0, ((lds_ci32*)(lds + 7 * kSlot))[lane]);
+        if (nb > 1) e1 = sanitise(1, ((lds_ci32*)(lds + 7 * kSlot + 256))[lane]);
+    }
     if (nb > 0) issue_part(0, e0);
     if (nb > 1) issue_part(1, e1);
     if (nb > 1) {
@@ -1311,11 +1386,12 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
             // s + 3)
             const int qtile = wave >> 1, qhalf = wave & 1;
             const bool issuing = s + 2 < nb;
-            const int e2 = issuing ? read_entries(s + 2) : -1;
+            int e2 = -1;
+            if (issuing) e2 = P ? prow_of(s + 2) : read_entries(s + 2);
             TileGather<false> tg = {};
             if (issuing) {
                 tg = plan_batch(s + 2, e2);
-                if (wave == 0 && s + 3 < nb) stage_entries(s + 3);
+                if (!P && wave == 0 && s + 3 < nb) stage_entries(s + 3);
                 issue_stage(tg, std::integral_constant<int, 0>{});
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1413,15 +1489,15 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
             const int vpos = lds_pos(8 * qg + (ln >> 1));
             const int r4 = ln >> 2, c4 = ln & 3;
             const int rpos0 = lds_pos(8 * qg + r4), rpos1 = lds_pos(8 * qg + 4 + r4);
-            f32x4 P[kPlTiles][2], S[kPlTiles][kNope][2];
+            f32x4 Pw[kPlTiles][2], S[kPlTiles][kNope][2];
             i32x2 V[kPlTiles][kNope][4];
             s16x4 R[kPlTiles][kRope ? 4 : 1][2];
 #pragma unroll
             for (int tt = 0; tt < kPlTiles; tt++) {
                 const lds_u8* st = st0 + tt * kSlot;
                 const lds_u8* pt = pt0 + tt * kPlPTile;
-                P[tt][0] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg));
-                P[tt][1] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg + 1));
+                Pw[tt][0] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg));
+                Pw[tt][1] = *(lds_cf32x4*)(pt + ptable_chunk(ln, 2 * qg + 1));
 #pragma unroll
                 for (int gi = 0; gi < kNope; gi++) {
                     const int g = 2 * vi + gi;
@@ -1461,12 +1537,12 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
 #pragma unroll
             for (int tt = 0; tt < kPlTiles; tt++) {
                 const float f = (qg >> 1) ? fh[2 * tt + 1] : fh[2 * tt];
-                P[tt][0] *= f;
-                P[tt][1] *= f;
+                Pw[tt][0] *= f;
+                Pw[tt][1] *= f;
             }
 #pragma unroll
             for (int tt = 0; tt < kPlTiles; tt++) {
-                const f32x4 p0 = P[tt][0], p1 = P[tt][1];
+                const f32x4 p0 = Pw[tt][0], p1 = Pw[tt][1];
 #pragma unroll
                 for (int gi = 0; gi < kNope; gi++) {
                     // weights fp16(p * scale), exact fp8 -> fp16 value codes
@@ -2016,27 +2092,39 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const dim3 g(grid), blk(64 * kWaves);
     (void)hipGetLastError();   // a launch error reported below is this launch's
     if (g_env.debug_validate && !launch_validate(a, hs)) return SMLA_ERR_HIP;
-    if (a.block_table != nullptr) {
+    // the pipelined kernel for split lists of up to kPipelinedMaxChunk entries
+    // (on a paged pool also at most kPlPagedBatches batches), unless
+    // SMLA_KERNEL chooses
+    const bool paged = a.block_table != nullptr;
+    const bool pipelined =
+        (g_env.kernel == 2 || (g_env.kernel == 0 && p.chunk <= kPipelinedMaxChunk)) &&
+        (!paged || (p.chunk <= kPlPagedBatches * kPlTiles * kTile &&
+                    (uint64_t)a.pool_rows * (uint64_t)row_bytes_of(a.row_format) < (1ull << 31)));
+    const int32_t remap = args.xcd_remap ? (int32_t)(grid / 8) : 0;
+    if (pipelined) {
+        const dim3 blk2(64 * kPlWaves);
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, g, blk2, 0, hs, args.kv, args.idx, args.seqlens, args.kv_seq_stride, args.topk,
+                               args.nsplit, args.chunk, args.n_hb, args.heads, remap, args);
+        };
+        if (a.row_format == SMLA_ROW_UE8M0_SCALES) {
+            if (paged) go(smla_decode_pipelined_kernel<SMLA_ROW_UE8M0_SCALES, true>);
+            else go(smla_decode_pipelined_kernel<SMLA_ROW_UE8M0_SCALES, false>);
+        } else {
+            if (paged) go(smla_decode_pipelined_kernel<SMLA_ROW_FP32_SCALES, true>);
+            else go(smla_decode_pipelined_kernel<SMLA_ROW_FP32_SCALES, false>);
+        }
+    } else if (paged) {
         if (!smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs)) return SMLA_ERR_HIP;
-    } else if (g_env.kernel == 1 || (g_env.kernel == 0 && p.chunk > kPipelinedMaxChunk)) {
+    } else {
         if (a.row_format == SMLA_ROW_UE8M0_SCALES)
             hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args.kv, args.idx,
                                args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
-                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
+                               args.heads, remap, args);
         else
             hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args.kv, args.idx,
                                args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
-                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
-    } else {
-        const dim3 blk2(64 * kPlWaves);
-        if (a.row_format == SMLA_ROW_UE8M0_SCALES)
-            hipLaunchKernelGGL((smla_decode_pipelined_kernel<SMLA_ROW_UE8M0_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
-                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
-                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
-        else
-            hipLaunchKernelGGL((smla_decode_pipelined_kernel<SMLA_ROW_FP32_SCALES>), g, blk2, 0, hs, args.kv, args.idx,
-                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
-                               args.heads, args.xcd_remap ? (int32_t)(grid / 8) : 0, args);
+                               args.heads, remap, args);
     }
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
