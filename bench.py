@@ -81,7 +81,8 @@ def counted_traffic(config, row_format):
     text = open(COUNTER_SUMMARY).read()
     digest = kernel_digest()
     m_src = re.search(r"code sha256\[:16\] = ([0-9a-f]{16})", text)
-    m_dec = re.search(r"decode kernel: FETCH_SIZE .*?-> ([0-9.]+) MB per launch; WRITE_SIZE .*?-> ([0-9.]+) MB", text)
+    m_dec = re.search(r"decode kernel(?: \([^)]*\))?: FETCH_SIZE .*?-> ([0-9.]+) MB per launch; WRITE_SIZE .*?-> ([0-9.]+) MB",
+                      text)
     if not m_src or not m_dec or m_src.group(1) != digest:
         return None
     return (float(m_dec.group(1)) + float(m_dec.group(2))) * 1e6

@@ -1,0 +1,24 @@
+"""bench.py's reading of the committed counter summary (host only): when the
+summary was taken on the current kernel source, the bench line's
+roofline.traffic must come from it, not silently read as null."""
+
+import re
+
+import pytest
+
+import bench
+
+
+def test_counter_summary_is_parsed_when_its_digest_matches():
+    text = open(bench.COUNTER_SUMMARY).read()
+    m = re.search(r"code sha256\[:16\] = ([0-9a-f]{16})", text)
+    assert m, "the counter summary names the kernel source it was taken on"
+    if m.group(1) != bench.kernel_digest():
+        pytest.skip("the kernel source changed since the counters were taken")
+    t = bench.counted_traffic(bench.COUNTER_CONFIG, 0)
+    assert t is not None and 1e6 < t < 1e9
+
+
+def test_counter_summary_only_for_its_own_workload():
+    assert bench.counted_traffic(bench.COUNTER_CONFIG + 1, 0) is None
+    assert bench.counted_traffic(bench.COUNTER_CONFIG, 1) is None
