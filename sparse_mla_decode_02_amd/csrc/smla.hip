@@ -1345,6 +1345,11 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
         if (nb > 1) e1 = sanitise(1, ((lds_ci32*)(lds + 7 * kSlot + 256))[lane]);
     }
     if (nb > 0) issue_part(0, e0);
+    // contiguous cache: every wave's gathers of batch 0 are issued before any
+    // of batch 1, so that the CU's address unit takes batch 0 first and it
+    // lands sooner (measured -0.45 us per step at 32 x 64 heads x top-512; on a
+    // paged pool, where the waves reach this point less evenly, +0.9 us)
+    if (!P && nb > 1) __builtin_amdgcn_s_barrier();
     if (nb > 1) issue_part(1, e1);
     if (nb > 1) {
         // at most this wave's gathers of batch 1 in flight
