@@ -1292,21 +1292,14 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
             for (int k = wave; k < n_copy; k += kPlWaves)
                 gather4(4u * (uint32_t)(64 * k + lane), btrsrc, lds_addr + 2 * kPlBatch + 256 * k);
         }
-        // every batch's entry loaded at once (clamped into the split's list:
-        // loads in per-batch branches would each wait for the one before)
-        int raw[kPlPagedBatches];
-        if (nb > 0) {
-#pragma unroll
-            for (int k = 0; k < kPlPagedBatches; k++) raw[k] = idx_b[min(k * kPlTiles * kTile + lane, n_ent - 1)];
-        }
-#pragma unroll
-        for (int k = 0; k < kPlPagedBatches; k++) pe[k] = k < nb ? sanitise(k, raw[k]) : -1;
-        wait_vmcnt<0>();   // the entries and this wave's share of the block-table row
-#pragma unroll
-        for (int k = 0; k < kPlPagedBatches; k++) asm volatile("" ::"v"(pe[k]));
-        // the query rows only now, so that no wait above includes them: they
-        // land while the first batches are gathered
+        // the entries of batch w into slot 7 by wave w (one copy per wave:
+        // the CU's address unit takes each request in turn, so few wide ones
+        // are issued sooner than one register load per batch and wave)
+        static_assert(kPlPagedBatches <= kPlWaves, "one entry copy per wave");
+        static_assert(kPlPagedBatches * kPlTiles * kTile * 4 <= kSlot, "the entries fit in slot 7");
+        if (wave < nb) gather4(4u * (uint32_t)(wave * kPlTiles * kTile + lane), irsrc, lds_addr + 7 * kSlot + 256 * wave);
         stage_query();
+        wait_vmcnt<2>();   // the entries and this wave's share of the block-table row (the query may be in flight)
     }
     // the pool rows of batch bt (a uniform index)
     auto prow_of = [&](int bt) -> int {
@@ -1320,6 +1313,9 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
     lds_barrier();     // the entries of batches 0..2 (paged: the block-table row) are visible
     int e0 = -1, e1 = -1;
     if constexpr (P) {
+#pragma unroll
+        for (int k = 0; k < kPlPagedBatches; k++)
+            pe[k] = k < nb ? sanitise(k, ((lds_ci32*)(lds + 7 * kSlot + 256 * k))[lane]) : -1;
         int pg[kPlPagedBatches], slot[kPlPagedBatches];
 #pragma unroll
         for (int k = 0; k < kPlPagedBatches; k++) slot[k] = pe[k] >= 0 ? min(pe[k] >> a.page_shift, a.pages_per_seq - 1) : 0;
