@@ -90,7 +90,6 @@ typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) const float lds_cf32;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) const f32x2 lds_cf32x2;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef __attribute__((address_space(3))) const int32_t lds_ci32;
@@ -1101,10 +1100,10 @@ constexpr int kPlLdsBytes = kPlPTable + 2 * kPlTiles * kPlPTile;
 static_assert(kPlLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 static_assert(16 * 1024 <= kScaleTable, "the staged query stays clear of its slot's scale table");
 static_assert(kPlBatch == 2 * kSlot, "slot k of the ring is slot k & 1 of buffer k >> 1");
-// the output rows of a workgroup's 16 heads, staged at the end in the first
-// batch buffer (free by then): row pitch 16 bytes above the row, so that the
-// sixteen rows start on sixteen different groups of four banks
-constexpr int kPlStagePitchBf16 = 2 * kLatent + 16;
+// the output rows of a workgroup's 16 heads (fp32, not yet normalised), staged
+// at the end in the first batch buffer (free by then): row pitch 16 bytes above
+// the row, so that the sixteen rows start on sixteen different groups of four
+// banks
 constexpr int kPlStagePitchF32 = 4 * kLatent + 16;
 static_assert(16 * kPlStagePitchF32 <= kPlBatch, "staged rows within the first batch buffer");
 static_assert(4 * kPlBtLds <= kPlBatch, "a paged prologue's block-table row fits the third batch buffer");
@@ -1363,33 +1362,48 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
     // step, then one for the weight sum), and each kind of value wave its own
     // copy of the value loop, so that a wave's registers keep their values
     // across the steps instead of being merged (copied) between code paths.
-    // ---- the end: the value waves stage their normalised columns in LDS, then
-    // all eight waves write the 16 rows in whole 1 KB pieces, 16 bytes per lane
-    // (a store instruction costs a wave about the same time whatever its width
-    // or address pattern, so few wide contiguous ones end the workgroup sooner)
+    // ---- the end: the value waves stage their columns in LDS (and the rope
+    // wave the weight sums), then after one barrier all eight waves normalise
+    // and write the 16 rows in whole 1 KB pieces, 16 bytes per lane (a store
+    // instruction costs a wave about the same time whatever its width or
+    // address pattern, so few wide contiguous ones end the workgroup sooner)
     const bool final_out = a.nsplit == 1 && !a.force_partials;
+    auto inv_sum = [&](int h) {   // 1 / (weight sum of row h), 0 for a row that kept nothing
+        const float l = ((lds_cf32*)stats_row(0, 0))[h];
+        return l > 0.f ? 1.f / l : 0.f;
+    };
     auto store_rows = [&]() {
         const int64_t bh0 = (int64_t)b * a.heads + 16 * hb;
         if (final_out) {
-            u32x4 v[2];
+            // rows 2w, 2w + 1; lane l: columns 8l..8l+7
+            f32x4 v[2][2];
 #pragma unroll
             for (int p = 0; p < 2; p++)
-                v[p] = *(lds_cu32x4*)(lds + (2 * wave + p) * kPlStagePitchBf16 + 16 * lane);
 #pragma unroll
-            for (int p = 0; p < 2; p++)
-                *(u32x4*)((uint8_t*)(a.out + (bh0 + 2 * wave + p) * kLatent) + 16 * lane) = v[p];
-        } else {
-            u32x4 v[4];
+                for (int j = 0; j < 2; j++)
+                    v[p][j] = *(lds_cf32x4*)(lds + (2 * wave + p) * kPlStagePitchF32 + 32 * lane + 16 * j);
 #pragma unroll
-            for (int p = 0; p < 4; p++) {
-                const int k = 4 * wave + p;   // head k >> 1, half k & 1 of its row
-                v[p] = *(lds_cu32x4*)(lds + (k >> 1) * kPlStagePitchF32 + 1024 * (k & 1) + 16 * lane);
+            for (int p = 0; p < 2; p++) {
+                const float inv = inv_sum(2 * wave + p);
+                const f32x4 x = v[p][0] * inv, y = v[p][1] * inv;
+                const u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
+                                 pack_bf16x2(y[2], y[3])};
+                *(u32x4*)((uint8_t*)(a.out + (bh0 + 2 * wave + p) * kLatent) + 16 * lane) = w;
             }
+        } else {
+            // pieces 4w..4w+3: head k >> 1, half k & 1 of its row
+            f32x4 v[4];
 #pragma unroll
             for (int p = 0; p < 4; p++) {
                 const int k = 4 * wave + p;
-                *(u32x4*)((uint8_t*)(a.o_part + ((bh0 + (k >> 1)) * a.nsplit + split) * kLatent) + 1024 * (k & 1) +
-                          16 * lane) = v[p];
+                v[p] = *(lds_cf32x4*)(lds + (k >> 1) * kPlStagePitchF32 + 1024 * (k & 1) + 16 * lane);
+            }
+            const float inv0 = inv_sum(2 * wave), inv1 = inv_sum(2 * wave + 1);
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                const int k = 4 * wave + p;
+                *(f32x4*)((uint8_t*)(a.o_part + ((bh0 + (k >> 1)) * a.nsplit + split) * kLatent) + 1024 * (k & 1) +
+                          16 * lane) = v[p] * (p < 2 ? inv0 : inv1);
             }
         }
     };
@@ -1500,8 +1514,7 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
             e1 = e2;
             lds_barrier();   // ends the step
         }
-        lds_barrier();   // the weight sum is written
-        lds_barrier();   // the output rows are staged
+        lds_barrier();   // the weight sums and the output rows are staged
         store_rows();
         return;
     }
@@ -1628,35 +1641,23 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
             lds_barrier();   // ends the step
         }
         // ---- the weight sum of head ln, from the rope wave's product with a
-        // column of ones (through a row that no gather writes)
+        // column of ones (through a row that no gather writes), and this
+        // wave's columns, not yet normalised, into the staged rows
         if constexpr (kRope)
             if (qg == 0) lsum[ln] = acc[8][0];
-        lds_barrier();
-        const float l_run = ((lds_cf32*)lsum)[ln];
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        const int64_t bh = (int64_t)b * a.heads + head;
+        {
+            lds_u8* const o = lds + ln * kPlStagePitchF32 + 4 * (128 * vi + 4 * qg);
+#pragma unroll
+            for (int c = 0; c < 8; c++) *(lds_f32x4*)(o + 64 * c) = acc[c];
+        }
+        lds_barrier();   // the weight sums and the output rows are staged
         if (vi == 0 && qg == 0) {
+            const float l_run = ((lds_cf32*)lsum)[ln];
             const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+            const int64_t bh = (int64_t)b * a.heads + head;
             if (final_out) a.lse[bh] = lse;
             else a.lse_part[bh * a.nsplit + split] = lse;
         }
-        // ---- normalise this wave's columns into the staged rows
-        if (final_out) {
-            lds_u8* const o = lds + ln * kPlStagePitchBf16 + 2 * (128 * vi + 4 * qg);
-#pragma unroll
-            for (int c = 0; c < 8; c++) {
-                u32x2 w;
-                const f32x4 v = acc[c] * inv;
-                w[0] = pack_bf16x2(v[0], v[1]);
-                w[1] = pack_bf16x2(v[2], v[3]);
-                *(lds_u32x2*)(o + 32 * c) = w;
-            }
-        } else {
-            lds_u8* const o = lds + ln * kPlStagePitchF32 + 4 * (128 * vi + 4 * qg);
-#pragma unroll
-            for (int c = 0; c < 8; c++) *(lds_f32x4*)(o + 64 * c) = acc[c] * inv;
-        }
-        lds_barrier();   // the output rows are staged
         store_rows();
     };
     if (vi < 3) value_loop(std::false_type{});
