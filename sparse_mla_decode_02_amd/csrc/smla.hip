@@ -1272,16 +1272,16 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
     if (!P) stage_query();
     // Paged pool: a kept entry e of the sequence is at pool row
     // (block_table[b][e >> page_shift] << page_shift) + (e & (page - 1)).  A
-    // split of this kernel holds at most kPlPagedBatches batches, so every
-    // lane translates its entry of each batch here, once, and keeps the pool
-    // rows in registers: lane l, batch k: tile l >> 5, position l & 31; -1 for
-    // a masked entry, a page past the table row or a slot outside the pool.
-    // The sequence's block-table row does not depend on the entries: up to
-    // kPlBtLds pages it is copied into the third batch buffer (free until step
-    // 0) while the entries load, so the translation costs no second memory
-    // round trip; a longer row is read entry by entry after the entries.
+    // split of this kernel holds at most kPlPagedBatches batches: wave k
+    // translates the entries of batch k here, once, and every wave then keeps
+    // the pool rows of every batch in registers: lane l, batch k: tile l >> 5,
+    // position l & 31; -1 for a masked entry, a page past the table row or a
+    // slot outside the pool.  The sequence's block-table row does not depend
+    // on the entries: up to kPlBtLds pages it is copied into the third batch
+    // buffer (free until step 0) while the entries load, so the translation
+    // costs no second memory round trip; a longer row is read entry by entry
+    // after the entries.
     int prow[P ? kPlPagedBatches : 1];
-    int pe[P ? kPlPagedBatches : 1];
     const int32_t* const bt_b = P ? a.block_table + (int64_t)b * a.pages_per_seq : nullptr;
     const bool bt_in_lds = P && a.pages_per_seq <= kPlBtLds;
     if constexpr (P) {
@@ -1312,27 +1312,25 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
     lds_barrier();     // the entries of batches 0..2 (paged: the block-table row) are visible
     int e0 = -1, e1 = -1;
     if constexpr (P) {
-#pragma unroll
-        for (int k = 0; k < kPlPagedBatches; k++)
-            pe[k] = k < nb ? sanitise(k, ((lds_ci32*)(lds + 7 * kSlot + 256 * k))[lane]) : -1;
-        int pg[kPlPagedBatches], slot[kPlPagedBatches];
-#pragma unroll
-        for (int k = 0; k < kPlPagedBatches; k++) slot[k] = pe[k] >= 0 ? min(pe[k] >> a.page_shift, a.pages_per_seq - 1) : 0;
-        if (bt_in_lds) {
-            const lds_ci32* const bt_lds = (lds_ci32*)(lds + 2 * kPlBatch);
-#pragma unroll
-            for (int k = 0; k < kPlPagedBatches; k++) pg[k] = bt_lds[slot[k]];
-        } else {
-#pragma unroll
-            for (int k = 0; k < kPlPagedBatches; k++) pg[k] = bt_b[slot[k]];   // all at once, as the entries
+        // wave w translates batch w (its entries in slot 7, one per lane) and
+        // writes the pool rows back in place; after a barrier every wave keeps
+        // every batch's pool rows in registers (slot 7 is gathered into from
+        // step 1 on)
+        lds_i32* const etab = (lds_i32*)(lds + 7 * kSlot);
+        {
+            const int k = wave;
+            const int e = k < nb ? sanitise(k, etab[64 * k + lane]) : -1;
+            const int sl = e >= 0 ? min(e >> a.page_shift, a.pages_per_seq - 1) : 0;
+            const int pg = bt_in_lds ? ((lds_ci32*)(lds + 2 * kPlBatch))[sl] : bt_b[sl];
+            const uint32_t page_mask = (1u << a.page_shift) - 1u;
+            etab[64 * k + lane] = k < nb && e >= 0 && (e >> a.page_shift) < a.pages_per_seq && pg >= 0 &&
+                                          (uint32_t)pg < (a.pool_rows >> a.page_shift)
+                                      ? (int)(((uint32_t)pg << a.page_shift) | ((uint32_t)e & page_mask))
+                                      : -1;
         }
-        const uint32_t page_mask = (1u << a.page_shift) - 1u;
+        lds_barrier();   // every batch's pool rows are in slot 7
 #pragma unroll
-        for (int k = 0; k < kPlPagedBatches; k++)
-            prow[k] = k < nb && pe[k] >= 0 && (pe[k] >> a.page_shift) < a.pages_per_seq && pg[k] >= 0 &&
-                              (uint32_t)pg[k] < (a.pool_rows >> a.page_shift)
-                          ? (int)(((uint32_t)pg[k] << a.page_shift) | ((uint32_t)pe[k] & page_mask))
-                          : -1;
+        for (int k = 0; k < kPlPagedBatches; k++) prow[k] = etab[64 * k + lane];
         e0 = prow[0];
         e1 = prow_of(1);
     } else {
