@@ -1845,12 +1845,15 @@ int log2_exact(int32_t v) {
 }
 
 constexpr int kComputeUnits = 256;   // MI355X; one workgroup per compute unit
-// Longest split list (entries per workgroup) taken by the pipelined kernel on
-// a contiguous cache; longer splits go to the four-wave kernel.  Measured on
-// MI355X (steps of the five benchmark workloads at split counts 1..8): the
-// pipelined kernel is ahead up to 512 entries (its fixed start-up is shorter),
-// the four-wave kernel from 1024 on (its waves stream their own tiles
-// without per-step barriers).
+// Longest split list (entries per workgroup) taken by the pipelined kernel for
+// UE8M0 rows and on a paged pool; longer splits go to the four-wave kernel.
+// Measured on MI355X (steps of the five benchmark workloads, three rounds):
+// with fp32 group scales on a contiguous cache the pipelined kernel is ahead
+// at every split length (1024 entries: 34.8-35.1 against 36.5-36.8 us; 2048:
+// 49.8-50.0 against 50.4-50.9), with UE8M0 rows the four-wave kernel from
+// 1024 entries on (39.4-39.5 against 39.9-40.2 us; 51.2-52.4 against
+// 53.2-54.0: the pipelined kernel expands the scale bytes in two of its logit
+// waves, the four-wave kernel in every wave).
 constexpr int kPipelinedMaxChunk = 512;
 constexpr int kMaxSplits = 4096;     // bound on the split count
 
@@ -1860,11 +1863,12 @@ constexpr int kMaxSplits = 4096;     // bound on the split count
 //   SMLA_DEBUG_VALIDATE=1   scan the device-resident inputs before every decode
 //   SMLA_KERNEL=four-wave | pipelined
 //                           contiguous-cache kernel for every shape, instead of
-//                           the choice by split length (kPipelinedMaxChunk)
+//                           the choice by row format and split length
+//                           (kPipelinedMaxChunk)
 struct EnvConfig {
     int nsplit;           // 0: the heuristic
     int debug_validate;
-    int kernel;           // 0: by split length, 1: four-wave, 2: pipelined
+    int kernel;           // 0: by row format and split length, 1: four-wave, 2: pipelined
 };
 
 EnvConfig read_env() {
@@ -2133,12 +2137,13 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const dim3 g(grid), blk(64 * kWaves);
     (void)hipGetLastError();   // a launch error reported below is this launch's
     if (g_env.debug_validate && !launch_validate(a, hs)) return SMLA_ERR_HIP;
-    // the pipelined kernel for split lists of up to kPipelinedMaxChunk entries
-    // (on a paged pool also at most kPlPagedBatches batches), unless
-    // SMLA_KERNEL chooses
+    // the pipelined kernel for fp32 group scales on a contiguous cache, and for
+    // split lists of up to kPipelinedMaxChunk entries otherwise (on a paged
+    // pool also at most kPlPagedBatches batches), unless SMLA_KERNEL chooses
     const bool paged = a.block_table != nullptr;
+    const bool by_default = p.chunk <= kPipelinedMaxChunk || (!paged && a.row_format == SMLA_ROW_FP32_SCALES);
     const bool pipelined =
-        (g_env.kernel == 2 || (g_env.kernel == 0 && p.chunk <= kPipelinedMaxChunk)) &&
+        (g_env.kernel == 2 || (g_env.kernel == 0 && by_default)) &&
         (!paged || (p.chunk <= kPlPagedBatches * kPlTiles * kTile &&
                     (uint64_t)a.pool_rows * (uint64_t)row_bytes_of(a.row_format) < (1ull << 31)));
     const int32_t remap = args.xcd_remap ? (int32_t)(grid / 8) : 0;

@@ -2,6 +2,9 @@
 the same seeded inputs.  Marked ``gpu``."""
 
 import functools
+import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -13,6 +16,7 @@ from tests._gpu import compare, device_inputs, log, run_decode
 from workloads import build_host_cache, config_workload, make_workload
 
 pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 @functools.lru_cache(maxsize=2)
@@ -42,9 +46,10 @@ def case_small(seed, **kw):
     return w, out, lse
 
 
-# Split lists of at most 512 entries run through the pipelined kernel, longer
-# ones through the four-wave kernel: configs 4 and 5 are run through both
-# ((4, 4), (4, 8), (5, 4) pipelined; (4, 0), (5, 0), (5, 3), (5, 1) four-wave).
+# A contiguous cache with fp32 group scales takes the pipelined kernel at every
+# split length; the four-wave kernel runs the same long lists in
+# test_four_wave_kernel_on_long_contiguous_lists (and the UE8M0 and paged ones
+# by default).
 CFG_SPLITS = [(1, 1), (1, 2), (1, 0), (2, 4), (2, 0), (3, 1), (3, 2), (3, 4), (3, 0),
               (4, 4), (4, 8), (4, 0), (5, 0), (5, 3), (5, 4), (5, 1)]
 
@@ -55,6 +60,22 @@ def test_config_parity(cfg, nsplit):
     w, ref_out, ref_lse = cfg_case(cfg)
     out, lse = run_decode(w, num_splits=nsplit)
     compare(out, lse, ref_out, ref_lse, label=f"cfg{cfg}/ns{nsplit}->{smla.num_splits(w.batch, w.heads, w.topk, nsplit)}")
+
+
+def test_four_wave_kernel_on_long_contiguous_lists(tmp_path):
+    # workloads 4 (two splits of 1024 entries) and 5 (one split) through the
+    # four-wave kernel, forced by SMLA_KERNEL in a child process
+    path = tmp_path / "four_wave.npz"
+    env = dict(os.environ, SMLA_KERNEL="four-wave", PYTHONPATH=ROOT)
+    log("starting the four-wave child process")
+    r = subprocess.run([sys.executable, "-u", "-m", "tests._kernel_child", str(path)], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=300)
+    log(r.stdout[-2000:])
+    assert r.returncode == 0, r.stderr[-3000:]
+    got = np.load(path)
+    for cfg in (4, 5):
+        w, ref_out, ref_lse = cfg_case(cfg)
+        compare(got[f"cfg{cfg}.out"], got[f"cfg{cfg}.lse"], ref_out, ref_lse, label=f"four-wave cfg{cfg}")
 
 
 @pytest.mark.parametrize("heads", [16, 32, 48, 64, 128])
