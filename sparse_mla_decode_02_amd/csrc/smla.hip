@@ -343,6 +343,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Block (sequence b, head block hb, split) of a decode workgroup: the XCD remap
+// (remap_stride = gridDim.x / 8, or 0) gives consecutive logical blocks the
+// same XCD, then the logical index splits as ((b * n_hb) + hb) * nsplit +
+// split.  Split and head-block counts that are powers of two (the usual ones)
+// take shifts and masks instead of the scalar division sequence (~50 scalar
+// instructions per wave, issued before the first memory request).
+__device__ __forceinline__ void block_coords(uint32_t bid, uint32_t remap_stride, int32_t nsplit, int32_t n_hb,
+                                             int& split, int& hb, int& b) {
+    if (remap_stride) bid = (bid & 7u) * remap_stride + (bid >> 3);
+    const uint32_t ns = (uint32_t)nsplit, nh = (uint32_t)n_hb;
+    uint32_t q;
+    if ((ns & (ns - 1u)) == 0u) {
+        split = (int)(bid & (ns - 1u));
+        q = bid >> __builtin_ctz(ns);
+    } else {
+        split = (int)(bid % ns);
+        q = bid / ns;
+    }
+    if ((nh & (nh - 1u)) == 0u) {
+        hb = (int)(q & (nh - 1u));
+        b = (int)(q >> __builtin_ctz(nh));
+    } else {
+        hb = (int)(q % nh);
+        b = (int)(q / nh);
+    }
+}
+
 struct DecodeArgs {
     const uint16_t* q;
     const uint8_t* kv;
@@ -827,12 +854,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
     const int qg = lane >> 4;                  // lane group 0..3
     const int ln = lane & 15;                  // head column of the 16x16 tiles
 
-    int bid = blockIdx.x;
-    if (remap_stride) bid = (bid & 7) * remap_stride + (bid >> 3);
-    const int split = bid % a.nsplit;
-    bid /= a.nsplit;
-    const int hb = bid % a.n_hb;
-    const int b = bid / a.n_hb;
+    int split, hb, b;
+    block_coords(blockIdx.x, remap_stride, a.nsplit, a.n_hb, split, hb, b);
 
     const int head = 16 * hb + ln;
     const int t_begin = split * a.chunk;
@@ -1154,12 +1177,8 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
     const int qg = lane >> 4;                  // lane group 0..3
     const int ln = lane & 15;                  // head column of the 16x16 tiles
 
-    int bid = blockIdx.x;
-    if (remap_stride) bid = (bid & 7) * remap_stride + (bid >> 3);
-    const int split = bid % a.nsplit;
-    bid /= a.nsplit;
-    const int hb = bid % a.n_hb;
-    const int b = bid / a.n_hb;
+    int split, hb, b;
+    block_coords(blockIdx.x, remap_stride, a.nsplit, a.n_hb, split, hb, b);
 
     const int head = 16 * hb + ln;
     const int t_begin = split * a.chunk;
