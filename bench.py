@@ -68,7 +68,7 @@ def kernel_digest() -> str:
     csrc = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc")
     text = "".join(open(os.path.join(csrc, f)).read() for f in sorted(os.listdir(csrc)) if f.endswith(".hip"))
     return code_digest(text + "\n// flags: " + " ".join(hip_build.HIPCC_FLAGS + hip_build.VGPR_FORM +
-                                                      hip_build.PRELOAD))
+                                                      hip_build.PRELOAD + hip_build.SCHED_ILP))
 
 
 def counted_traffic(config, row_format):

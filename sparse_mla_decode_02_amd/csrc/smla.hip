@@ -745,7 +745,7 @@ __device__ __forceinline__ void combine_row(const float* o_part, const float* ls
     if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
-#ifndef SMLA_PAGED_TU
+#if !defined(SMLA_PAGED_TU) && !defined(SMLA_FOURWAVE_TU)
 // The combine as its own kernel: one wave per (b, h), four rows per
 // workgroup.  When the grid is a multiple of 8, workgroup ids are remapped like
 // the decode kernel's, so that XCD x merges the rows of the same contiguous
@@ -1828,7 +1828,7 @@ __global__ __launch_bounds__(256) void smla_per_head_kernel(PerHeadArgs a) {
     if (lane == 0) a.lse[bh] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
-#ifndef SMLA_PAGED_TU
+#if !defined(SMLA_PAGED_TU) && !defined(SMLA_FOURWAVE_TU)
 struct Plan {
     int n_hb;     // 16-head blocks (workgroups per sequence and split)
     int nsplit;
@@ -2027,6 +2027,13 @@ void* scratch_for_current_device() {
 __attribute__((visibility("hidden"))) bool smla_launch_paged_decode(const void* args, size_t bytes,
                                                                     int row_format, unsigned grid,
                                                                     hipStream_t hs);
+// The contiguous-cache instances of the four-wave kernel likewise (included by
+// smla_fourwave.hip with SMLA_FOURWAVE_TU): this unit's pipelined kernel is
+// scheduled for instruction-level parallelism, which measured faster for it
+// (build.py) and slower for the four-wave kernel.
+__attribute__((visibility("hidden"))) bool smla_launch_fourwave_decode(const void* args, size_t bytes,
+                                                                       int row_format, unsigned grid,
+                                                                       hipStream_t hs);
 
 #ifdef SMLA_PAGED_TU
 bool smla_launch_paged_decode(const void* args, size_t bytes, int row_format, unsigned grid, hipStream_t hs) {
@@ -2042,6 +2049,21 @@ bool smla_launch_paged_decode(const void* args, size_t bytes, int row_format, un
         hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, true>), g, blk, 0, hs, a.kv, a.idx, a.seqlens,
                            a.kv_seq_stride, a.topk, a.nsplit, a.chunk, a.n_hb, a.heads,
                            a.xcd_remap ? (int32_t)(grid / 8) : 0, a);
+    return true;
+}
+#elif defined(SMLA_FOURWAVE_TU)
+bool smla_launch_fourwave_decode(const void* args, size_t bytes, int row_format, unsigned grid, hipStream_t hs) {
+    DecodeArgs a;
+    if (bytes != sizeof(a)) return false;
+    memcpy(&a, args, sizeof(a));
+    const dim3 g(grid), blk(64 * kWaves);
+    const int32_t remap = a.xcd_remap ? (int32_t)(grid / 8) : 0;
+    if (row_format == SMLA_ROW_UE8M0_SCALES)
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, a.kv, a.idx,
+                           a.seqlens, a.kv_seq_stride, a.topk, a.nsplit, a.chunk, a.n_hb, a.heads, remap, a);
+    else
+        hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, a.kv, a.idx,
+                           a.seqlens, a.kv_seq_stride, a.topk, a.nsplit, a.chunk, a.n_hb, a.heads, remap, a);
     return true;
 }
 #else
@@ -2153,7 +2175,7 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     const int grid = a.batch * p.n_hb * p.nsplit;
     DecodeArgs args = a;
     args.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    const dim3 g(grid), blk(64 * kWaves);
+    const dim3 g(grid);
     (void)hipGetLastError();   // a launch error reported below is this launch's
     if (g_env.debug_validate && !launch_validate(a, hs)) return SMLA_ERR_HIP;
     // the pipelined kernel for fp32 group scales on a contiguous cache, and for
@@ -2182,14 +2204,7 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     } else if (paged) {
         if (!smla_launch_paged_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs)) return SMLA_ERR_HIP;
     } else {
-        if (a.row_format == SMLA_ROW_UE8M0_SCALES)
-            hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_UE8M0_SCALES, false>), g, blk, 0, hs, args.kv, args.idx,
-                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
-                               args.heads, remap, args);
-        else
-            hipLaunchKernelGGL((smla_decode_kernel<SMLA_ROW_FP32_SCALES, false>), g, blk, 0, hs, args.kv, args.idx,
-                               args.seqlens, args.kv_seq_stride, args.topk, args.nsplit, args.chunk, args.n_hb,
-                               args.heads, remap, args);
+        if (!smla_launch_fourwave_decode(&args, sizeof(args), a.row_format, (unsigned)grid, hs)) return SMLA_ERR_HIP;
     }
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }

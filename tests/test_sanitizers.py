@@ -16,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE_C = os.path.join(ROOT, "oracle", "oracle.c")
 SMLA_HIP = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc", "smla.hip")
 SMLA_PAGED_HIP = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc", "smla_paged.hip")
+SMLA_FOURWAVE_HIP = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc", "smla_fourwave.hip")
 INCLUDE = os.path.join(ROOT, "include")
 
 ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1",
@@ -161,7 +162,7 @@ def test_c_abi_host_code_under_address_and_undefined_behaviour_sanitizers(tmp_pa
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
     objs = []
-    for src in (SMLA_HIP, SMLA_PAGED_HIP):
+    for src in (SMLA_HIP, SMLA_FOURWAVE_HIP, SMLA_PAGED_HIP):
         objs.append(tmp_path / (os.path.basename(src) + ".o"))
         rc, log = _run([_hipcc(), "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", *san,
                         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-c", src, "-o", str(objs[-1])])
