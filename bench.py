@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library heuristic")
     ap.add_argument("--kernel", default="shared", choices=("shared", "per-head"),
                     help="shared: the decode path; per-head: the per-head SIMT ablation kernel")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="time sparse_mla_decode_single_launch: split partials merged inside the decode kernel")
     ap.add_argument("--page-size", type=int, default=0,
                     help="0 = contiguous cache; else rows in a shuffled paged pool of this page size")
     ap.add_argument("--page-order", default="shuffled", choices=("shuffled", "sequential"),
@@ -262,6 +264,13 @@ def main():
         full_args = [(P(q), P(cache), P(idx), P(sl), ctypes.c_float(w.scale), P(out), P(lse), ctypes.byref(shape), hs)
                      for q, cache, idx, sl, _ in sets]
         decode_fn = L.sparse_mla_decode_per_head
+    if args.single_launch:
+        assert args.kernel == "shared", "the single launch is a form of the shared-read path"
+        counters = torch.zeros(B * (H // 16), dtype=torch.int32, device=dev)   # arrival counters, left at zero
+        full_args = [(P(q), P(cache), P(bt) if paged else None, P(idx), P(sl), ctypes.c_float(w.scale), P(out),
+                      P(lse), ctypes.byref(shape), ctypes.byref(pg) if paged else None, wsp,
+                      ctypes.c_size_t(need_ws), P(counters), hs) for q, cache, idx, sl, bt in sets]
+        decode_fn = L.sparse_mla_decode_single_launch
 
     def step(i):
         """One whole step: decode kernel, then the combine kernel when split."""
@@ -269,8 +278,9 @@ def main():
         assert st == 0, st
 
     def decode_only(i):
-        """The decode kernel alone (split partials when the list is split)."""
-        if ns == 1:
+        """The decode kernel alone (split partials when the list is split; the
+        whole step in the single launch)."""
+        if ns == 1 or args.single_launch:
             st = decode_fn(*full_args[i % R])
         else:
             st = partials_fn(*dec_args[i % R])
@@ -320,10 +330,15 @@ def main():
     # and each step's own duration (events around every step, rotated inputs)
     warm_ms, _ = timed(lambda i: step(0), args.steps)
     # KV cold, q / list / lengths warm: rotated caches, the first copy's other inputs
+    # (topk_idx and seqlens follow the block table in the paged and single-launch
+    # signatures; checked on the host against the first copy before any launch)
+    pos = 3 if (paged or args.single_launch) else 2
+    assert full_args[0][0].value == sets[0][0].data_ptr()
+    assert full_args[0][pos].value == sets[0][2].data_ptr() and full_args[0][pos + 1].value == sets[0][3].data_ptr()
     kvcold_args = []
-    for q, cache, idx, sl, bt in sets:
-        a = list(full_args[len(kvcold_args)])
-        a[0], a[2 if not paged else 3], a[3 if not paged else 4] = (P(sets[0][0]), P(sets[0][2]), P(sets[0][3]))
+    for a in full_args:
+        a = list(a)
+        a[0], a[pos], a[pos + 1] = P(sets[0][0]), P(sets[0][2]), P(sets[0][3])
         kvcold_args.append(tuple(a))
     kvcold_ms, _ = timed(lambda i: decode_fn(*kvcold_args[i % R]), args.steps)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -385,10 +400,12 @@ def main():
                    "row_format": "ue8m0_scales_584B" if fmt == 1 else "fp32_scales_640B",
                    "cache": (f"paged, {args.page_size} rows per page, {args.page_order} pages" if paged
                              else "contiguous per sequence"),
-                   "kernel": "per-head SIMT ablation" if args.kernel == "per-head" else "shared-read MFMA",
+                   "kernel": ("per-head SIMT ablation" if args.kernel == "per-head" else
+                              "shared-read MFMA, single launch" if args.single_launch else "shared-read MFMA"),
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": None if paged else counted_traffic(args.config, fmt)},
+                     "frac": kv_gbps / HBM_PEAK_GBPS,
+                     "traffic": None if (paged or args.single_launch) else counted_traffic(args.config, fmt)},
         "cpu_baseline": cpu,
         "effective_kv_gbps": kv_gbps,
         "all_algorithmic_gbps": all_bytes / t_dec / 1e9,

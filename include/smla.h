@@ -209,6 +209,44 @@ smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool,
                                              float* o_part, float* lse_part, void* stream);
 
 /*
+ * sparse_mla_decode_single_launch -- sparse_mla_decode (or, with paged set,
+ * sparse_mla_decode_paged) as one kernel launch.  The pages deploy the kernel
+ * under CUDA-graph capture ("The Power-of-Two Trap", section "The Aftermath:
+ * Validation and Deployment"); with the list split, the combine of the split
+ * partials then runs inside the decode kernel instead of as a second launch:
+ * the last of a (sequence, 16-head block)'s splits to finish merges every
+ * split's partial (as sparse_mla_combine does) into out and lse.
+ *
+ *   q, topk_idx, seqlens, scale, out, lse, shape: as for sparse_mla_decode
+ *   kv_cache    the contiguous cache, or with paged != NULL the pool
+ *   block_table with paged != NULL, as for sparse_mla_decode_paged (ignored
+ *               otherwise)
+ *   paged       NULL for a contiguous cache, else as for sparse_mla_decode_paged
+ *   workspace, workspace_bytes: as for sparse_mla_decode (the split partials)
+ *   counters    uint32 [B][H / 16], 4-byte aligned device memory: one arrival
+ *               counter per (sequence, 16-head block); may be NULL when the
+ *               shape resolves to one split.  Every counter a call uses must be
+ *               zero when it starts (e.g. allocate the array zeroed once, for
+ *               the largest B x H / 16 it will serve); every call that runs to
+ *               completion leaves them zero, so one array serves any later
+ *               call, shape and graph replay.  Calls that share counters or a
+ *               workspace must not run at the same time.
+ *   stream      as for sparse_mla_decode
+ *
+ * Errors as for sparse_mla_decode / sparse_mla_decode_paged, plus
+ * SMLA_ERR_NULL / SMLA_ERR_ALIGN for the counters of a split shape.  The
+ * results are bitwise those of sparse_mla_decode (the same partials, merged
+ * by the same arithmetic); a shape that resolves to one split is the same
+ * launch as sparse_mla_decode's.
+ */
+smla_status sparse_mla_decode_single_launch(const void* q, const void* kv_cache,
+                                            const int32_t* block_table, const int32_t* topk_idx,
+                                            const int32_t* seqlens, float scale, void* out,
+                                            float* lse, const smla_shape* shape,
+                                            const smla_paged* paged, void* workspace,
+                                            size_t workspace_bytes, uint32_t* counters, void* stream);
+
+/*
  * sparse_mla_decode_per_head -- the same step computed the way the production
  * kernel that the shared-read design replaced did it ("The Moment of
  * Compilation", section "The Context: A Kernel Optimization Campaign"): one

@@ -33,7 +33,8 @@ NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024   # SMLA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine", "sparse_mla_decode_noalloc",
            "sparse_mla_decode_paged", "sparse_mla_decode_partials_paged", "sparse_mla_decode_per_head",
-           "smla_workspace_bytes", "smla_num_splits", "smla_split_size", "smla_status_str",
+           "sparse_mla_decode_single_launch", "smla_workspace_bytes",
+           "smla_num_splits", "smla_split_size", "smla_status_str",
            "smla_debug_validate_enabled", "smla_debug_flags")
 
 # condition bits of the SMLA_DEBUG_VALIDATE input scan (smla.h)
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_decode_paged.restype = ctypes.c_int
         L.sparse_mla_decode_partials_paged.argtypes = [vp, vp, vp, vp, vp, f32, shp, pgd, vp, vp, vp]
         L.sparse_mla_decode_partials_paged.restype = ctypes.c_int
+        L.sparse_mla_decode_single_launch.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, shp, pgd, vp,
+                                                      ctypes.c_size_t, vp, vp]
+        L.sparse_mla_decode_single_launch.restype = ctypes.c_int
         L.smla_debug_validate_enabled.argtypes = []
         L.smla_debug_validate_enabled.restype = i32
         L.smla_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
@@ -223,6 +227,44 @@ def sparse_mla_combine(o_part, lse_part, out, lse, *, stream=None):
     B, H, S, _ = o_part.shape
     _check(lib().sparse_mla_combine(_ptr(o_part), _ptr(lse_part), B, H, S, _ptr(out), _ptr(lse),
                                     _stream_handle(stream)))
+    return out, lse
+
+
+def sparse_mla_decode_single_launch(q, kv_cache, topk_idx, seqlens, scale, out, lse, *, num_splits=0,
+                                    kv_seq_stride=None, block_table=None, page_size=None, num_pages=None,
+                                    workspace=None, counters=None, stream=None, row_format=0):
+    """sparse_mla_decode (block_table None) or sparse_mla_decode_paged (block_table
+    and page_size given) as one kernel launch: the last split of each head block
+    merges the partials.  counters: uint32/int32 device tensor of at least
+    B * H / 16 elements, zero before its first use (allocated zeroed here when
+    None); each completed call leaves it zero.  workspace as for
+    sparse_mla_decode."""
+    import torch
+    B, H, _ = q.shape
+    topk = topk_idx.shape[1] if topk_idx.dim() == 2 else 0
+    paged = None
+    if block_table is not None:
+        if num_pages is None:
+            num_pages = kv_cache.numel() // (ROW_BYTES_OF_FORMAT.get(row_format, ROW_BYTES) * page_size)
+        paged = make_paged(page_size, block_table.shape[1], num_pages)
+        kv_seq_stride = 1
+    elif kv_seq_stride is None:
+        kv_seq_stride = _seq_stride(kv_cache, B, row_format)
+    shape = make_shape(B, H, topk, num_splits, kv_seq_stride, row_format)
+    L = lib()
+    need = int(L.smla_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if counters is None and need > 0:
+        counters = torch.zeros(max(B * (H // 16), 1), dtype=torch.int32, device=q.device)
+    if counters is not None:
+        assert counters.numel() * counters.element_size() >= 4 * B * (H // 16), "counters: B * H / 16 words"
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.sparse_mla_decode_single_launch(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(topk_idx),
+                                             _ptr(seqlens), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                             ctypes.byref(shape), ctypes.byref(paged) if paged is not None else None,
+                                             _ptr(workspace), ctypes.c_size_t(ws_bytes), _ptr(counters),
+                                             _stream_handle(stream)))
     return out, lse
 
 

@@ -391,6 +391,9 @@ struct DecodeArgs {
     int32_t page_shift;       // log2 rows per page
     int32_t pages_per_seq;
     uint32_t pool_rows;       // num_pages << page_shift (< 2^32)
+    // single-launch merge: one arrival counter per (sequence, head block),
+    // zero between launches (nullptr: the combine runs as its own kernel)
+    uint32_t* arrive;
 };
 
 // Gather one whole 32-token tile into the LDS slot at slot_lds.  Lane l holds
@@ -745,6 +748,46 @@ __device__ __forceinline__ void combine_row(const float* o_part, const float* ls
     if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
+// Single-launch merge.  The split partials go out as device-scope stores
+// (store16_device / store4_device: written through the XCD's L2, which keeps no
+// dirty copy of them), so that the one agent-scope release fence below has
+// nothing of theirs to write back.  After its partial stores every wave waits
+// for them to complete; then wave 0 takes the release fence and counts the
+// workgroup in at its (sequence, head block) counter.  The last of the nsplit
+// workgroups to arrive takes an agent-scope acquire fence in every wave,
+// merges the 16 heads' partials of every split (combine_row: each wave a row
+// at a time) into the output rows and lse, and puts the counter back to zero
+// for the next launch.  No workgroup waits for another, so the grid drains in
+// any dispatch order.  flag: an LDS word no wave reads or writes after its
+// partial stores.
+__device__ __forceinline__ void store16_device(float* base, uint32_t range, uint32_t off, f32x4 v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)range, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 16 /* sc1 */);
+}
+
+__device__ __forceinline__ void store4_device(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int b, int hb, int wave, int nwaves, int lane,
+                                              lds_u32* flag) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    uint32_t* const ctr = a.arrive + (int64_t)b * a.n_hb + hb;
+    if (wave == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0)
+            *flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (uint32_t)(a.nsplit - 1);
+    }
+    __syncthreads();
+    if (!*flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int64_t bh0 = (int64_t)b * a.heads + 16 * hb;
+    for (int h = wave; h < 16; h += nwaves) combine_row(a.o_part, a.lse_part, bh0 + h, a.nsplit, a.out, a.lse, lane);
+    if (wave == 0 && lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 #if !defined(SMLA_PAGED_TU) && !defined(SMLA_FOURWAVE_TU)
 // The combine as its own kernel: one wave per (b, h), four rows per
 // workgroup.  When the grid is a multiple of 8, workgroup ids are remapped like
@@ -1063,6 +1106,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
             w[1] = pack_bf16x2(v[2], v[3]);
             *(u32x2*)(o + 16 * (i0 + ii)) = w;
         }
+    } else if (a.arrive) {
+        // single launch: device-scope stores from the workgroup's first row
+        const int64_t bh0 = (int64_t)b * a.heads + 16 * hb;
+        float* const base = a.o_part + (bh0 * a.nsplit + split) * kLatent;
+        const uint32_t row_off = (uint32_t)(ln * a.nsplit) * (kLatent * 4) + 16 * qg;
+#pragma unroll
+        for (int ii = 0; ii < 32 / kWaves; ii++)
+            store16_device(base, 16u * (uint32_t)a.nsplit * (kLatent * 4), row_off + 64 * (i0 + ii),
+                           block_sum(i0 + ii));
     } else {
         float* o = a.o_part + (bh * a.nsplit + split) * kLatent + 4 * qg;
 #pragma unroll
@@ -1070,8 +1122,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
     }
     if (wave == 0 && qg == 0) {
         if (final_out) a.lse[bh] = lse2 * kLn2;
+        else if (a.arrive) store4_device(a.lse_part + bh * a.nsplit + split, lse2 * kLn2);
         else a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
     }
+    if (a.arrive) merge_if_last(a, b, hb, wave, kWaves, lane, (lds_u32*)lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1416,11 +1470,23 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
                 v[p] = *(lds_cf32x4*)(lds + (k >> 1) * kPlStagePitchF32 + 1024 * (k & 1) + 16 * lane);
             }
             const float inv0 = inv_sum(2 * wave), inv1 = inv_sum(2 * wave + 1);
+            if (a.arrive) {
+                // single launch: device-scope stores from the workgroup's first row
+                float* const base = a.o_part + (bh0 * a.nsplit + split) * kLatent;
 #pragma unroll
-            for (int p = 0; p < 4; p++) {
-                const int k = 4 * wave + p;
-                *(f32x4*)((uint8_t*)(a.o_part + ((bh0 + (k >> 1)) * a.nsplit + split) * kLatent) + 1024 * (k & 1) +
-                          16 * lane) = v[p] * (p < 2 ? inv0 : inv1);
+                for (int p = 0; p < 4; p++) {
+                    const int k = 4 * wave + p;
+                    store16_device(base, 16u * (uint32_t)a.nsplit * (kLatent * 4),
+                                   (uint32_t)((k >> 1) * a.nsplit) * (kLatent * 4) + 1024 * (k & 1) + 16 * lane,
+                                   v[p] * (p < 2 ? inv0 : inv1));
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < 4; p++) {
+                    const int k = 4 * wave + p;
+                    *(f32x4*)((uint8_t*)(a.o_part + ((bh0 + (k >> 1)) * a.nsplit + split) * kLatent) +
+                              1024 * (k & 1) + 16 * lane) = v[p] * (p < 2 ? inv0 : inv1);
+                }
             }
         }
     };
@@ -1533,6 +1599,7 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
         }
         lds_barrier();   // the weight sums and the output rows are staged
         store_rows();
+        if (a.arrive) merge_if_last(a, b, hb, wave, kPlWaves, lane, (lds_u32*)(lds + kPlPTable));
         return;
     }
 
@@ -1673,9 +1740,11 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
             const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
             const int64_t bh = (int64_t)b * a.heads + head;
             if (final_out) a.lse[bh] = lse;
+            else if (a.arrive) store4_device(a.lse_part + bh * a.nsplit + split, lse);
             else a.lse_part[bh * a.nsplit + split] = lse;
         }
         store_rows();
+        if (a.arrive) merge_if_last(a, b, hb, wave, kPlWaves, lane, (lds_u32*)(lds + kPlPTable));
     };
     if (vi < 3) value_loop(std::false_type{});
     else value_loop(std::true_type{});
@@ -2209,10 +2278,14 @@ static smla_status launch(const DecodeArgs& a, const Plan& p, hipStream_t hs) {
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
+// single: a split shape merges its partials in the decode kernel (the last
+// split of each head block to finish, counted at counters), with no combine
+// launch
 static smla_status decode_impl(const void* q, const void* kv_cache, const int32_t* block_table,
                                const int32_t* topk_idx, const int32_t* seqlens, float scale, void* out,
                                float* lse, const smla_shape* shape, const smla_paged* paged,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, void* stream, bool single = false,
+                               uint32_t* counters = nullptr) {
     DecodeArgs a;
     Plan p;
     bool nothing;
@@ -2221,6 +2294,10 @@ static smla_status decode_impl(const void* q, const void* kv_cache, const int32_
     if (!out || !lse) return SMLA_ERR_NULL;
     if (!aligned(out, 16) || !aligned(lse, 4)) return SMLA_ERR_ALIGN;
     const size_t need = workspace_for(shape, p);
+    if (single && p.nsplit > 1) {
+        if (!counters) return SMLA_ERR_NULL;
+        if (!aligned(counters, 4)) return SMLA_ERR_ALIGN;
+    }
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return SMLA_ERR_ALIGN;
@@ -2233,11 +2310,12 @@ static smla_status decode_impl(const void* q, const void* kv_cache, const int32_
         const WorkspaceLayout w = workspace_layout(shape, p);
         a.o_part = (float*)workspace;
         a.lse_part = (float*)((char*)workspace + w.lse_off);
+        if (single) a.arrive = counters;
     }
     hipStream_t hs = (hipStream_t)stream;
     st = launch(a, p, hs);
     if (st != SMLA_OK) return st;
-    if (p.nsplit > 1) {
+    if (p.nsplit > 1 && !single) {
         const int rws = shape->batch * shape->num_heads;
         hipLaunchKernelGGL(smla_combine_kernel, dim3((rws + 3) / 4), dim3(256), 0, hs, a.o_part,
                            a.lse_part, rws, p.nsplit, (uint16_t*)out, lse);
@@ -2287,6 +2365,15 @@ smla_status sparse_mla_decode_paged(const void* q, const void* kv_pool, const in
     if (!paged) return SMLA_ERR_NULL;
     return decode_impl(q, kv_pool, block_table, topk_idx, seqlens, scale, out, lse, shape, paged, workspace,
                        workspace_bytes, stream);
+}
+
+smla_status sparse_mla_decode_single_launch(const void* q, const void* kv_cache, const int32_t* block_table,
+                                            const int32_t* topk_idx, const int32_t* seqlens, float scale,
+                                            void* out, float* lse, const smla_shape* shape,
+                                            const smla_paged* paged, void* workspace, size_t workspace_bytes,
+                                            uint32_t* counters, void* stream) {
+    return decode_impl(q, kv_cache, paged ? block_table : nullptr, topk_idx, seqlens, scale, out, lse, shape,
+                       paged, workspace, workspace_bytes, stream, true, counters);
 }
 
 smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool, const int32_t* block_table,

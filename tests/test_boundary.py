@@ -231,3 +231,38 @@ def test_noalloc_argument_errors_before_any_device_work():
     if not torch.cuda.is_available():
         assert call(fits) == 7                                        # valid, but no device here
         assert call(fits, out=None) in (1, 7)
+
+
+@needs_lib
+def test_single_launch_argument_errors():
+    L = smla.lib()
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(shape, paged=None, ws=None, wsb=0, **over):
+        a = dict(q=fake, kv=fake, bt=fake, idx=fake, sl=fake, out=fake, lse=fake, ctr=ctypes.c_void_p(1 << 22))
+        a.update(over)
+        return L.sparse_mla_decode_single_launch(
+            a["q"], a["kv"], a["bt"], a["idx"], a["sl"], ctypes.c_float(0.05), a["out"], a["lse"],
+            ctypes.byref(shape) if shape is not None else None, ctypes.byref(paged) if paged is not None else None,
+            ws, ctypes.c_size_t(wsb), a["ctr"], None)
+    split = smla.make_shape(2, 16, 64, 2, 128)
+    need = L.smla_workspace_bytes(ctypes.byref(split))      # the same split partials as sparse_mla_decode
+    assert need > 0
+    ws = ctypes.c_void_p(1 << 21)
+    assert call(None) == 1                                                  # NULL shape
+    assert call(split, ws=ws, wsb=need, out=None) == 1                      # NULL operand
+    assert call(smla.make_shape(2, 20, 64, 2, 128)) == 2                    # H not a multiple of 16
+    assert call(split, ws=ws, wsb=need, ctr=None) == 1                      # counters missing
+    assert call(split, ws=ws, wsb=need, ctr=ctypes.c_void_p((1 << 22) + 2)) == 6   # counters misaligned
+    assert call(split) == 4                                                 # workspace missing
+    assert call(split, ws=ws, wsb=need - 1) == 4
+    assert call(split, ws=ctypes.c_void_p((1 << 21) + 16), wsb=need) == 6   # workspace misaligned
+    paged = smla.make_paged(64, 4, 16)
+    assert call(split, paged, bt=None, ws=ws, wsb=need) == 1               # no block table
+    assert call(split, smla.make_paged(48, 4, 16), ws=ws, wsb=need) == 2    # page size not a power of two
+    one = smla.make_shape(2, 16, 64, 1, 128)
+    import torch
+    if not torch.cuda.is_available():
+        assert call(split, ws=ws, wsb=need) == 7                           # valid, but no device here
+        assert call(split, paged, ws=ws, wsb=need) == 7
+        assert call(one, ctr=None) == 7                                     # one split: no counters needed
