@@ -697,55 +697,77 @@ __device__ __forceinline__ void pin_state(bf16x8 (&qop)[16], f32x4 (&acc_o)[32])
     for (int k = 0; k < 32; k++) asm volatile("" : "+a"(acc_o[k]));
 }
 
-// Log-sum-exp merge of the split partials of one (b, h) row by one wave, 8
-// columns per lane.  Splits are taken four at a time: the four log-sum-exps
-// (scalar loads) and partial outputs (vector loads) of a group are all issued
-// before any is used, so a row with at most four splits costs one round trip
-// to memory; later groups are folded in with a running-maximum rescale.  Split
-// indices past the end are clamped and given weight 0.  An empty split (lse =
-// -inf) has weight exp(-inf) = 0 and a zero partial.
-__device__ __forceinline__ void combine_row(const float* o_part, const float* lse_part, int64_t row,
-                                            int nsplit, uint16_t* out, float* lse, int lane) {
-    const float* lp = lse_part + row * nsplit;
-    const float* src = o_part + row * nsplit * kLatent + 8 * lane;
-    float M = -INFINITY, W = 0.f;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
-        float l[4];
-        f32x4 lo[4], hi[4];
+// Log-sum-exp merge of the split partials of R (b, h) rows (row0 + k * rstep)
+// by one wave, 8 columns per lane.  Splits are taken four at a time: the four
+// log-sum-exps (scalar loads) and partial outputs (vector loads) of a group
+// are issued for all R rows before any is used, so R rows with at most four
+// splits cost one round trip to memory; later groups are folded in with a
+// running-maximum rescale.  Each row's arithmetic is the same for every R.
+// (Issuing the next group's loads before folding in this one measured slower,
+// in the combine kernel and in the single-launch merge.)
+// Split indices past the end are clamped and given weight 0.  An empty split
+// (lse = -inf) has weight exp(-inf) = 0 and a zero partial.
+template <int R>
+__device__ __forceinline__ void combine_rows(const float* o_part, const float* lse_part, int64_t row0,
+                                             int64_t rstep, int nsplit, uint16_t* out, float* lse, int lane) {
+    float M[R], W[R];
+    f32x4 acc0[R], acc1[R];
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int sk = min(s0 + k, nsplit - 1);
-            l[k] = lp[sk];
-            lo[k] = *(const f32x4*)(src + sk * kLatent);
-            hi[k] = *(const f32x4*)(src + sk * kLatent + 4);
-        }
-        float m = M;
-#pragma unroll
-        for (int k = 0; k < 4; k++)
-            if (s0 + k < nsplit) m = fmaxf(m, l[k]);
-        const float ms = m == -INFINITY ? 0.f : m;
-        const float f = __expf(M - ms);   // 0 while nothing was folded in
-        W *= f;
-        acc0 *= f;
-        acc1 *= f;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const float w = s0 + k < nsplit ? __expf(l[k] - ms) : 0.f;
-            W += w;
-            acc0 += w * lo[k];
-            acc1 += w * hi[k];
-        }
-        M = m;
+    for (int r = 0; r < R; r++) {
+        M[r] = -INFINITY;
+        W[r] = 0.f;
+        acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    u32x4 pk;
-    pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
-    pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
-    pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
-    pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
-    *(u32x4*)(out + row * kLatent + 8 * lane) = pk;
-    if (lane == 0) lse[row] = W > 0.f ? M + logf(W) : -INFINITY;
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+        float l[R][4];
+        f32x4 lo[R][4], hi[R][4];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int64_t row = row0 + r * rstep;
+            const float* lp = lse_part + row * nsplit;
+            const float* src = o_part + row * nsplit * kLatent + 8 * lane;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int sk = min(s0 + k, nsplit - 1);
+                l[r][k] = lp[sk];
+                lo[r][k] = *(const f32x4*)(src + sk * kLatent);
+                hi[r][k] = *(const f32x4*)(src + sk * kLatent + 4);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            float m = M[r];
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                if (s0 + k < nsplit) m = fmaxf(m, l[r][k]);
+            const float ms = m == -INFINITY ? 0.f : m;
+            const float f = __expf(M[r] - ms);   // 0 while nothing was folded in
+            W[r] *= f;
+            acc0[r] *= f;
+            acc1[r] *= f;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float w = s0 + k < nsplit ? __expf(l[r][k] - ms) : 0.f;
+                W[r] += w;
+                acc0[r] += w * lo[r][k];
+                acc1[r] += w * hi[r][k];
+            }
+            M[r] = m;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int64_t row = row0 + r * rstep;
+        const float inv = W[r] > 0.f ? 1.f / W[r] : 0.f;
+        u32x4 pk;
+        pk[0] = pack_bf16x2(acc0[r][0] * inv, acc0[r][1] * inv);
+        pk[1] = pack_bf16x2(acc0[r][2] * inv, acc0[r][3] * inv);
+        pk[2] = pack_bf16x2(acc1[r][0] * inv, acc1[r][1] * inv);
+        pk[3] = pack_bf16x2(acc1[r][2] * inv, acc1[r][3] * inv);
+        *(u32x4*)(out + row * kLatent + 8 * lane) = pk;
+        if (lane == 0) lse[row] = W[r] > 0.f ? M[r] + logf(W[r]) : -INFINITY;
+    }
 }
 
 // Single-launch merge.  The split partials go out as device-scope stores
@@ -753,11 +775,14 @@ __device__ __forceinline__ void combine_row(const float* o_part, const float* ls
 // dirty copy of them), so that the one agent-scope release fence below has
 // nothing of theirs to write back.  After its partial stores every wave waits
 // for them to complete; then wave 0 takes the release fence and counts the
-// workgroup in at its (sequence, head block) counter.  The last of the nsplit
-// workgroups to arrive takes an agent-scope acquire fence in every wave,
-// merges the 16 heads' partials of every split (combine_row: each wave a row
-// at a time) into the output rows and lse, and puts the counter back to zero
-// for the next launch.  No workgroup waits for another, so the grid drains in
+// workgroup in at its (sequence, head block) counter.  In the last of the
+// nsplit workgroups to arrive, wave 0 takes an agent-scope acquire fence and a
+// workgroup barrier orders every wave's loads after it (the fence invalidates
+// the XCD's L2, so once per workgroup: once per wave cost the other
+// workgroups on the XCD their cached rows, ~4.5 us per step at 32 x 64 heads);
+// then the workgroup merges the 16 heads' partials of every split
+// (combine_rows: each wave its 16 / NWAVES rows together) into the output
+// rows and lse, and puts the counter back to zero for the next launch.  No workgroup waits for another, so the grid drains in
 // any dispatch order.  flag: an LDS word no wave reads or writes after its
 // partial stores.
 __device__ __forceinline__ void store16_device(float* base, uint32_t range, uint32_t off, f32x4 v) {
@@ -769,8 +794,8 @@ __device__ __forceinline__ void store4_device(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int b, int hb, int wave, int nwaves, int lane,
-                                              lds_u32* flag) {
+template <int NWAVES>
+__device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int b, int hb, int wave, int lane, lds_u32* flag) {
     wait_vmcnt<0>();
     __syncthreads();
     uint32_t* const ctr = a.arrive + (int64_t)b * a.n_hb + hb;
@@ -782,9 +807,10 @@ __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int b, int hb
     }
     __syncthreads();
     if (!*flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (wave == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
     const int64_t bh0 = (int64_t)b * a.heads + 16 * hb;
-    for (int h = wave; h < 16; h += nwaves) combine_row(a.o_part, a.lse_part, bh0 + h, a.nsplit, a.out, a.lse, lane);
+    combine_rows<16 / NWAVES>(a.o_part, a.lse_part, bh0 + wave, NWAVES, a.nsplit, a.out, a.lse, lane);
     if (wave == 0 && lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -801,7 +827,7 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(const float* o_part, 
     if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
     const int row = bid * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
-    combine_row(o_part, lse_part, row, nsplit, out, lse, threadIdx.x & 63);
+    combine_rows<1>(o_part, lse_part, row, 0, nsplit, out, lse, threadIdx.x & 63);
 }
 
 // Debug scan of the device-resident inputs, launched ahead of the decode
@@ -1125,7 +1151,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void smla_decode_kernel(const uint8
         else if (a.arrive) store4_device(a.lse_part + bh * a.nsplit + split, lse2 * kLn2);
         else a.lse_part[bh * a.nsplit + split] = lse2 * kLn2;
     }
-    if (a.arrive) merge_if_last(a, b, hb, wave, kWaves, lane, (lds_u32*)lds);
+    if (a.arrive) merge_if_last<kWaves>(a, b, hb, wave, lane, (lds_u32*)lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1599,7 +1625,7 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
         }
         lds_barrier();   // the weight sums and the output rows are staged
         store_rows();
-        if (a.arrive) merge_if_last(a, b, hb, wave, kPlWaves, lane, (lds_u32*)(lds + kPlPTable));
+        if (a.arrive) merge_if_last<kPlWaves>(a, b, hb, wave, lane, (lds_u32*)(lds + kPlPTable));
         return;
     }
 
@@ -1744,7 +1770,7 @@ __global__ __launch_bounds__(64 * kPlWaves) void smla_decode_pipelined_kernel(co
             else a.lse_part[bh * a.nsplit + split] = lse;
         }
         store_rows();
-        if (a.arrive) merge_if_last(a, b, hb, wave, kPlWaves, lane, (lds_u32*)(lds + kPlPTable));
+        if (a.arrive) merge_if_last<kPlWaves>(a, b, hb, wave, lane, (lds_u32*)(lds + kPlPTable));
     };
     if (vi < 3) value_loop(std::false_type{});
     else value_loop(std::true_type{});
