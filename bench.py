@@ -88,6 +88,17 @@ def counted_traffic(config, row_format):
     return (float(m_dec.group(1)) + float(m_dec.group(2))) * 1e6
 
 
+# Positions of q, topk_idx and seqlens in the argument tuple of each C entry
+# point that bench.py times (tests/test_bench_records.py checks them against
+# include/smla.h).
+ENTRY_ARG_POS = {
+    "sparse_mla_decode": (0, 2, 3),
+    "sparse_mla_decode_paged": (0, 3, 4),
+    "sparse_mla_decode_single_launch": (0, 3, 4),
+    "sparse_mla_decode_per_head": (0, 2, 3),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,15 +341,15 @@ def main():
     # and each step's own duration (events around every step, rotated inputs)
     warm_ms, _ = timed(lambda i: step(0), args.steps)
     # KV cold, q / list / lengths warm: rotated caches, the first copy's other inputs
-    # (topk_idx and seqlens follow the block table in the paged and single-launch
-    # signatures; checked on the host against the first copy before any launch)
-    pos = 3 if (paged or args.single_launch) else 2
-    assert full_args[0][0].value == sets[0][0].data_ptr()
-    assert full_args[0][pos].value == sets[0][2].data_ptr() and full_args[0][pos + 1].value == sets[0][3].data_ptr()
+    # (the positions by entry point; checked on the host against the first copy
+    # before any launch)
+    qp, ip, sp = ENTRY_ARG_POS[decode_fn.__name__]
+    assert full_args[0][qp].value == sets[0][0].data_ptr()
+    assert full_args[0][ip].value == sets[0][2].data_ptr() and full_args[0][sp].value == sets[0][3].data_ptr()
     kvcold_args = []
     for a in full_args:
         a = list(a)
-        a[0], a[pos], a[pos + 1] = P(sets[0][0]), P(sets[0][2]), P(sets[0][3])
+        a[qp], a[ip], a[sp] = P(sets[0][0]), P(sets[0][2]), P(sets[0][3])
         kvcold_args.append(tuple(a))
     kvcold_ms, _ = timed(lambda i: decode_fn(*kvcold_args[i % R]), args.steps)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]

@@ -22,3 +22,18 @@ def test_counter_summary_is_parsed_when_its_digest_matches():
 def test_counter_summary_only_for_its_own_workload():
     assert bench.counted_traffic(bench.COUNTER_CONFIG + 1, 0) is None
     assert bench.counted_traffic(bench.COUNTER_CONFIG, 1) is None
+
+
+def test_entry_argument_positions_match_the_header():
+    # the KV-cold loop of bench.py swaps q, topk_idx and seqlens into prebuilt
+    # argument tuples by position: the positions must be those of include/smla.h
+    import os
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "smla.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    for name, (qp, ip, sp) in bench.ENTRY_ARG_POS.items():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", hdr)
+        assert m, name
+        params = [p.strip().split()[-1].lstrip("*") for p in m.group(1).split(",")]
+        assert params[qp] == "q", (name, params)
+        assert params[ip] == "topk_idx", (name, params)
+        assert params[sp] == "seqlens", (name, params)
