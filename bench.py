@@ -67,8 +67,10 @@ def kernel_digest() -> str:
     from sparse_mla_decode_02_amd import build as hip_build
     csrc = os.path.join(ROOT, "sparse_mla_decode_02_amd", "csrc")
     text = "".join(open(os.path.join(csrc, f)).read() for f in sorted(os.listdir(csrc)) if f.endswith(".hip"))
-    return code_digest(text + "\n// flags: " + " ".join(hip_build.HIPCC_FLAGS + hip_build.VGPR_FORM +
-                                                      hip_build.PRELOAD + hip_build.SCHED_ILP))
+    # the flags as a line of their own (not a comment, which code_digest drops)
+    flags = hip_build.HIPCC_FLAGS + hip_build.VGPR_FORM + hip_build.PRELOAD + hip_build.SCHED_ILP + \
+        hip_build.SCHED_CLAUSE
+    return code_digest(text + "\nflags: " + " ".join(flags))
 
 
 def counted_traffic(config, row_format):

@@ -37,6 +37,11 @@ PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=10"]
 # contiguous instances (smla_fourwave.hip) and the paged ones (smla_paged.hip)
 # keep the default scheduler.
 SCHED_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+# The four-wave contiguous unit is scheduled to keep memory instructions in
+# clauses: 0.4 us less decode at 96 x 16 heads x top-2048 in UE8M0 rows, the
+# same at 64 x 64 heads; on the paged unit it measured 0.8 us slower at
+# 64 x 64 heads, so that unit keeps the default.
+SCHED_CLAUSE = ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]
 
 
 def hipcc() -> str:
@@ -67,8 +72,8 @@ def build(verbose: bool = False, extra: list | None = None) -> str:
         obj_paged = os.path.join(tmp_dir, "smla_paged.o")
         _run([hipcc(), *HIPCC_FLAGS, *VGPR_FORM, *PRELOAD, *SCHED_ILP, *(extra or []), "-c", SRC, "-o", obj_main],
              verbose)
-        _run([hipcc(), *HIPCC_FLAGS, *VGPR_FORM, *PRELOAD, *(extra or []), "-c", SRC_FOURWAVE, "-o", obj_fourwave],
-             verbose)
+        _run([hipcc(), *HIPCC_FLAGS, *VGPR_FORM, *PRELOAD, *SCHED_CLAUSE, *(extra or []), "-c", SRC_FOURWAVE, "-o",
+              obj_fourwave], verbose)
         _run([hipcc(), *HIPCC_FLAGS, *PRELOAD, *(extra or []), "-c", SRC_PAGED, "-o", obj_paged], verbose)
         tmp = LIB + ".tmp" + tag
         _run([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", obj_main, obj_fourwave, obj_paged, "-o", tmp],

@@ -37,3 +37,15 @@ def test_entry_argument_positions_match_the_header():
         assert params[qp] == "q", (name, params)
         assert params[ip] == "topk_idx", (name, params)
         assert params[sp] == "seqlens", (name, params)
+
+
+def test_kernel_digest_follows_the_build_flags(monkeypatch):
+    # the profiles' code hash must change with a compiler flag, not only with
+    # the kernel sources (a comment edit keeps it)
+    from sparse_mla_decode_02_amd import build as hip_build
+    d0 = bench.kernel_digest()
+    monkeypatch.setattr(hip_build, "SCHED_CLAUSE", [])
+    assert bench.kernel_digest() != d0
+    monkeypatch.undo()
+    assert bench.kernel_digest() == d0
+    assert bench.code_digest("int a; // x\n/* y */\n\nint b;") == bench.code_digest("int a;\nint b;")
