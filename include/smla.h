@@ -233,12 +233,18 @@ smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool,
  *               workspace must not run at the same time.
  *   stream      as for sparse_mla_decode
  *
+ * With shape->num_splits 0 the split count is smla_num_splits_single_launch
+ * (shape): at most sparse_mla_decode's, as the in-kernel merge costs more
+ * than the combine kernel (32 sequences x 64 heads x top-512 runs as one
+ * split), so the workspace sparse_mla_decode needs always suffices.
+ *
  * Errors as for sparse_mla_decode / sparse_mla_decode_paged, plus
  * SMLA_ERR_NULL / SMLA_ERR_ALIGN for the counters of a split shape.  The
- * results are bitwise those of sparse_mla_decode (the same partials, merged
- * by the same arithmetic); a shape that resolves to one split is the same
- * launch as sparse_mla_decode's.
+ * results are bitwise those of sparse_mla_decode with the same split count
+ * (the same partials, merged by the same arithmetic); a shape that resolves
+ * to one split is the same launch as sparse_mla_decode's.
  */
+int32_t smla_num_splits_single_launch(const smla_shape* shape);
 smla_status sparse_mla_decode_single_launch(const void* q, const void* kv_cache,
                                             const int32_t* block_table, const int32_t* topk_idx,
                                             const int32_t* seqlens, float scale, void* out,

@@ -33,7 +33,7 @@ NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024   # SMLA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("sparse_mla_decode", "sparse_mla_decode_partials", "sparse_mla_combine", "sparse_mla_decode_noalloc",
            "sparse_mla_decode_paged", "sparse_mla_decode_partials_paged", "sparse_mla_decode_per_head",
-           "sparse_mla_decode_single_launch", "smla_workspace_bytes",
+           "sparse_mla_decode_single_launch", "smla_num_splits_single_launch", "smla_workspace_bytes",
            "smla_num_splits", "smla_split_size", "smla_status_str",
            "smla_debug_validate_enabled", "smla_debug_flags")
 
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_decode_single_launch.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, shp, pgd, vp,
                                                       ctypes.c_size_t, vp, vp]
         L.sparse_mla_decode_single_launch.restype = ctypes.c_int
+        L.smla_num_splits_single_launch.argtypes = [shp]
+        L.smla_num_splits_single_launch.restype = i32
         L.smla_debug_validate_enabled.argtypes = []
         L.smla_debug_validate_enabled.restype = i32
         L.smla_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
@@ -134,6 +136,11 @@ def make_shape(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format
 def num_splits(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> int:
     s = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride, row_format)
     return int(lib().smla_num_splits(ctypes.byref(s)))
+
+
+def num_splits_single_launch(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> int:
+    shape = make_shape(batch, num_heads, topk, num_splits, kv_seq_stride, row_format)
+    return int(lib().smla_num_splits_single_launch(ctypes.byref(shape)))
 
 
 def split_size(batch, num_heads, topk, num_splits=0, kv_seq_stride=1, row_format=0) -> int:

@@ -2008,8 +2008,13 @@ const EnvConfig g_env = read_env();
 // paths); a launch costs that times the number of rounds of kComputeUnits
 // workgroups; a split list adds one tile time for the partials and the
 // combine plus a fifth per four splits the combine merges.  Ties go to fewer
-// splits.
-int choose_splits(int base, int tiles) {
+// splits.  For the single launch (single) a split list adds 3.25 tile times
+// plus a fifth per split instead: the in-kernel merge (device-scope stores,
+// the fences and the counter, then one workgroup reading every split's
+// partial) costs more than the combine kernel, and more per split.  Its
+// penalty over the combine's grows with the split count, so it never picks
+// more splits than the two-launch model, and the same workspace suffices.
+int choose_splits(int base, int tiles, bool single = false) {
     if (base <= 0 || tiles <= 1) return 1;
     int best = 1;
     long best_cost = -1;
@@ -2018,7 +2023,8 @@ int choose_splits(int base, int tiles) {
         if (ns > 1 && (tiles + per_block - 1) / per_block < ns) continue;   // same chunks as fewer splits
         const long rounds = ((long)base * ns + kComputeUnits - 1) / kComputeUnits;
         const long block = 40L * ((per_block + kWaves - 1) / kWaves + 3) + 5L * per_block;
-        const long cost = rounds * block + (ns > 1 ? 40L + 8L * ((ns + 3) / 4) : 0L);
+        const long split_cost = single ? 130L + 8L * ns : 40L + 8L * ((ns + 3) / 4);
+        const long cost = rounds * block + (ns > 1 ? split_cost : 0L);
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
             best = ns;
@@ -2027,12 +2033,12 @@ int choose_splits(int base, int tiles) {
     return best;
 }
 
-Plan make_plan(const smla_shape* s) {
+Plan make_plan(const smla_shape* s, bool single = false) {
     Plan p;
     p.n_hb = s->num_heads / 16;
     const int tiles = (s->topk + kTile - 1) / kTile;
     int ns = s->num_splits;
-    if (ns == 0) ns = g_env.nsplit > 0 ? g_env.nsplit : choose_splits(s->batch * p.n_hb, tiles);
+    if (ns == 0) ns = g_env.nsplit > 0 ? g_env.nsplit : choose_splits(s->batch * p.n_hb, tiles, single);
     if (ns > tiles) ns = tiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
@@ -2170,6 +2176,11 @@ int32_t smla_num_splits(const smla_shape* shape) {
     return make_plan(shape).nsplit;
 }
 
+int32_t smla_num_splits_single_launch(const smla_shape* shape) {
+    if (!shape_ok(shape)) return -1;
+    return make_plan(shape, true).nsplit;
+}
+
 size_t smla_workspace_bytes(const smla_shape* shape) {
     if (!shape_ok(shape)) return 0;
     return workspace_for(shape, make_plan(shape));
@@ -2210,7 +2221,7 @@ smla_status sparse_mla_combine(const float* o_part, const float* lse_part, int32
 static smla_status prepare(const void* q, const void* kv_cache, const int32_t* topk_idx,
                            const int32_t* seqlens, float scale, const smla_shape* shape,
                            const smla_paged* paged, const int32_t* block_table,
-                           DecodeArgs* a, Plan* p, bool* nothing) {
+                           DecodeArgs* a, Plan* p, bool* nothing, bool single = false) {
     *nothing = false;
     if (!shape) return SMLA_ERR_NULL;
     if (!shape_ok(shape) || (paged && !paged_ok(paged))) return SMLA_ERR_SHAPE;
@@ -2224,7 +2235,7 @@ static smla_status prepare(const void* q, const void* kv_cache, const int32_t* t
     if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(topk_idx, 4) || !aligned(seqlens, 4) ||
         !aligned(block_table, 4))
         return SMLA_ERR_ALIGN;
-    *p = make_plan(shape);
+    *p = make_plan(shape, single);
     memset(a, 0, sizeof(*a));
     a->q = (const uint16_t*)q;
     a->kv = (const uint8_t*)kv_cache;
@@ -2315,7 +2326,8 @@ static smla_status decode_impl(const void* q, const void* kv_cache, const int32_
     DecodeArgs a;
     Plan p;
     bool nothing;
-    smla_status st = prepare(q, kv_cache, topk_idx, seqlens, scale, shape, paged, block_table, &a, &p, &nothing);
+    smla_status st = prepare(q, kv_cache, topk_idx, seqlens, scale, shape, paged, block_table, &a, &p, &nothing,
+                             single);
     if (st != SMLA_OK || nothing) return st;
     if (!out || !lse) return SMLA_ERR_NULL;
     if (!aligned(out, 16) || !aligned(lse, 4)) return SMLA_ERR_ALIGN;

@@ -234,6 +234,23 @@ def test_noalloc_argument_errors_before_any_device_work():
 
 
 @needs_lib
+def test_single_launch_split_choice():
+    # the single launch's model on the five benchmark workloads (its fastest
+    # measured split counts on MI355X: 1, 4, 1, 2, 1), never more splits than
+    # sparse_mla_decode's (whose workspace it uses), and -1 for invalid shapes
+    shapes = [(1, 16, 64, 256), (4, 16, 512, 8192), (32, 64, 512, 32768), (96, 16, 2048, 65536),
+              (64, 64, 2048, 131072)]
+    assert [smla.num_splits_single_launch(B, H, k, 0, S) for B, H, k, S in shapes] == [1, 4, 1, 2, 1]
+    import random
+    rng = random.Random(7)
+    for _ in range(3000):
+        B, H, k = rng.randint(1, 128), 16 * rng.randint(1, 16), rng.randint(1, 8192)
+        assert 1 <= smla.num_splits_single_launch(B, H, k, 0, k) <= smla.num_splits(B, H, k, 0, k)
+    assert smla.num_splits_single_launch(2, 16, 64, 2, 128) == 2      # a request is kept
+    assert smla.num_splits_single_launch(1, 15, 64) == -1
+
+
+@needs_lib
 def test_single_launch_argument_errors():
     L = smla.lib()
     fake = ctypes.c_void_p(1 << 20)

@@ -62,9 +62,11 @@ def as_np(out, lse):
 
 
 def check(w, inputs, ns, ref_out, ref_lse, label, ws=None, ctr=None):
-    """single launch == sparse_mla_decode bit for bit, and within tolerance of the oracle"""
+    """single launch == sparse_mla_decode with the same resolved split count,
+    bit for bit, and within tolerance of the oracle"""
     out, lse = run_single(w, inputs, ns, ws=ws, ctr=ctr)
-    two_out, two_lse = run_decode(w, inputs, num_splits=ns)
+    res = smla.num_splits_single_launch(w.batch, w.heads, inputs[2].shape[1], ns, w.kv_seq_stride, w.row_format)
+    two_out, two_lse = run_decode(w, inputs, num_splits=res)
     o, l = as_np(out, lse)
     assert np.array_equal(o, two_out, equal_nan=True), label
     assert np.array_equal(l, two_lse, equal_nan=True), label
@@ -73,16 +75,17 @@ def check(w, inputs, ns, ref_out, ref_lse, label, ws=None, ctr=None):
 
 # (workload, row format, split request): the pipelined kernel on every row
 # format up to 512 entries per split and on fp32 scales beyond; the four-wave
-# kernel on the longer UE8M0 splits
-CASES = [(2, 0, 0), (3, 0, 0), (3, 0, 4), (3, 1, 0), (4, 0, 0), (4, 1, 2), (5, 0, 3)]
+# kernel on the longer UE8M0 splits; 0 = the single launch's own choice
+# (4, 1, 2 and 1 splits at workloads 2, 3, 4 and 5)
+CASES = [(2, 0, 0), (3, 0, 0), (3, 0, 2), (3, 0, 4), (3, 1, 2), (4, 0, 0), (4, 1, 2), (5, 0, 3)]
 
 
 @pytest.mark.parametrize("cfg,row_format,nsplit", CASES)
 def test_single_launch_config_parity(cfg, row_format, nsplit):
     log(f"case: single launch config {cfg} row format {row_format} num_splits {nsplit}")
     w, ref_out, ref_lse = cfg_case(cfg, row_format)
-    ns = smla.num_splits(w.batch, w.heads, w.topk, nsplit, w.kv_seq_stride, row_format)
-    assert ns > 1
+    ns = smla.num_splits_single_launch(w.batch, w.heads, w.topk, nsplit, w.kv_seq_stride, row_format)
+    assert ns <= smla.num_splits(w.batch, w.heads, w.topk, nsplit, w.kv_seq_stride, row_format)
     check(w, device_inputs(w), nsplit, ref_out, ref_lse, f"single cfg{cfg}/f{row_format}/ns{ns}")
 
 
@@ -185,7 +188,7 @@ def device_paged_inputs(w, lay):
     return q, pool, bt, torch.from_numpy(w.idx).to(DEV), torch.from_numpy(w.seqlens).to(DEV)
 
 
-@pytest.mark.parametrize("cfg,row_format,nsplit", [(3, 1, 0), (4, 1, 2)])
+@pytest.mark.parametrize("cfg,row_format,nsplit", [(3, 1, 2), (4, 1, 2)])
 def test_single_launch_paged(cfg, row_format, nsplit):
     # the deployed layout (UE8M0 rows in a pool of 64-row pages): the pipelined
     # kernel's paged instance at workload 3, the four-wave one at workload 4;
