@@ -234,7 +234,7 @@ smla_status sparse_mla_decode_partials_paged(const void* q, const void* kv_pool,
  *   stream      as for sparse_mla_decode
  *
  * With shape->num_splits 0 the split count is smla_num_splits_single_launch
- * (shape): at most sparse_mla_decode's, as the in-kernel merge costs more
+ * (shape) (-1 for a NULL or invalid shape): at most sparse_mla_decode's, as the in-kernel merge costs more
  * than the combine kernel (32 sequences x 64 heads x top-512 runs as one
  * split), so the workspace sparse_mla_decode needs always suffices.
  *
