@@ -214,3 +214,17 @@ def test_single_launch_one_split_is_the_plain_launch():
     w, ref_out, ref_lse = small_case(55, batch=4, heads=16, topk=200, seqlen=1000)
     assert smla.workspace_bytes(w.batch, w.heads, w.topk, 1, w.kv_seq_stride) == 0
     check(w, device_inputs(w), 1, ref_out, ref_lse, "single ns1")
+
+
+def test_single_launch_many_splits_and_heads():
+    # 256 heads (16 head blocks, 16 counters per sequence) and 32 splits of a
+    # 4096-entry list: the merging workgroup folds in eight groups of four
+    w, ref_out, ref_lse = small_case(57, batch=2, heads=256, topk=4096, seqlen=5000)
+    assert smla.num_splits_single_launch(w.batch, w.heads, w.topk, 32, w.kv_seq_stride) == 32
+    inputs = device_inputs(w)
+    ctr = torch.zeros(w.batch * w.heads // 16, dtype=torch.int32, device=DEV)
+    for rep in range(2):
+        log(f"case: single launch 256 heads 32 splits #{rep}")
+        check(w, inputs, 32, ref_out, ref_lse, f"single H256 ns32 #{rep}", ctr=ctr)
+        torch.cuda.synchronize()
+        assert int(ctr.abs().sum()) == 0
