@@ -3,6 +3,9 @@ scales): libsmla.so through its C ABI against the fp64 CPU oracle on the same
 seeded inputs.  Marked ``gpu``."""
 
 import functools
+import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -14,6 +17,7 @@ from tests._gpu import compare, device_inputs, log, run_decode
 from workloads import ROW_FMT_UE8M0, build_host_cache, config_workload, make_workload
 
 pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def oracle_ref(w):
@@ -152,3 +156,20 @@ def test_ue8m0_partials_match_oracle_splits():
     assert np.abs(l[fin] - ref_l[fin]).max() <= 1e-3
     assert np.abs(o - ref_o).max() <= 1e-2 * max(1.0, np.abs(ref_o).max() / 4)
     assert np.linalg.norm(o - ref_o) / np.linalg.norm(ref_o) <= 5e-3
+
+
+def test_pipelined_kernel_on_long_ue8m0_lists(tmp_path):
+    # workloads 4 (two splits of 1024 entries) and 5 (one split) in UE8M0 rows
+    # through the pipelined kernel (the four-wave kernel runs them by
+    # default), forced by SMLA_KERNEL in a child process
+    path = tmp_path / "pipelined_ue8m0.npz"
+    env = dict(os.environ, SMLA_KERNEL="pipelined", PYTHONPATH=ROOT)
+    log("starting the pipelined UE8M0 child process")
+    r = subprocess.run([sys.executable, "-u", "-m", "tests._kernel_child", str(path), "1"], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=300)
+    log(r.stdout[-2000:])
+    assert r.returncode == 0, r.stderr[-3000:]
+    got = np.load(path)
+    for cfg in (4, 5):
+        w, ref_out, ref_lse = cfg_case(cfg)
+        compare(got[f"cfg{cfg}.out"], got[f"cfg{cfg}.lse"], ref_out, ref_lse, label=f"pipelined ue8m0 cfg{cfg}")
